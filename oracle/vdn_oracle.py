@@ -1,0 +1,305 @@
+"""fp64 CPU oracle of the Video DeltaNet (VDN) hybrid video-to-video attention layer.
+
+TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the benchmark's CPU
+baseline may import this module; the library and its Python binding never do,
+and this module imports nothing from them.
+
+It computes, in float64 with NumPy, exactly what the layer is defined to compute:
+
+  * the frame partition of every query frame into a softmax key set S(i), a
+    forward linear set Phi(i) and a backward linear set Psi(i)
+    [sd114.wiki article "VDN-Minimax-H3 ...", sections 双向滑动窗口Softmax分支 and
+    双向线性注意力分支; ananclaw note "Video DeltaNet ... critical read", section
+    一、方法拆解];
+  * the softmax branch: softmax(q k^T / sqrt(d)) v over all tokens of S(i)
+    [same sd114.wiki section 双向滑动窗口Softmax分支];
+  * the Video Delta Attention (VDA) state update, once per frame, with all of
+    the frame's tokens jointly solving one update that is non-expansive
+    [besthub article "VDN-H3 Generates 14-Second 768p Video ...", section
+    Video Delta Attention (VDA); arXiv abstract page "Video DeltaNet: A
+    Video-Native Hybrid Attention ...", Abstract].  The pages do not print the
+    algebra; the form used is the proximal least-squares step
+    S_t = (S_{t-1} + beta V_t K_t^T)(I + beta K_t K_t^T)^-1;
+  * the bidirectional readout o = S_fwd q + S_bwd q (the query reads both states
+    and the results are added) [sd114.wiki section 双向线性注意力分支];
+  * the gated merge O = O_soft + g * O_lin [arXiv abstract: separate output
+    projections and learnable gates calibrate the two branches; besthub section
+    Hybrid Attention Architecture: outputs merged by a gating mechanism].
+
+Tensor layout: q, k, v are [F, N, H, d] (frame, token-in-frame, head, channel);
+beta is [F, H]; gate is [H, d]; states are [C, H, d, d] with C = ceil(F / 5),
+row index = value channel, column index = key channel.
+
+Readings taken where the pages are silent (each is listed with its reason in the
+design notes): initial state zero; forward scan starts at frame 1 and the
+backward scan at frame F-2 (anchors excluded); the same beta in both directions;
+edge chunks see only the chunks that exist (no inward shift); softmax scale
+1/sqrt(d); anchor query frames have no linear output; additive merge with a
+per-(head, channel) gate; no normaliser in the linear readout.
+
+Parity unpinned: that the VDA algebra above is the authors' update (the pages do
+not give it), and the fp8 (e4m3) softmax variant beyond the quantiser itself.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+CHUNK_FRAMES = 5          # five latent frames per chunk
+E4M3_MAX = 448.0          # largest finite OCP E4M3 ("FN") value
+
+
+# --------------------------------------------------------------------------
+# Frame partition
+# --------------------------------------------------------------------------
+
+def chunk_of(i: int) -> int:
+    return i // CHUNK_FRAMES
+
+
+def num_chunks(F: int) -> int:
+    return (F + CHUNK_FRAMES - 1) // CHUNK_FRAMES
+
+
+def is_anchor(i: int, F: int) -> bool:
+    """First and last frame are the boundary anchors."""
+    return i == 0 or i == F - 1
+
+
+def window_frames(c: int, F: int) -> list[int]:
+    """Frames of chunk c and of its previous and next chunk (those that exist)."""
+    return [j for j in range(F) if abs(chunk_of(j) - c) <= 1]
+
+
+def softmax_frames(i: int, F: int) -> list[int]:
+    """Key frames whose tokens query frame i attends to with softmax.
+
+    Anchor query frames (first, last) see every frame; any other frame sees its
+    chunk window plus all tokens of the first and last frames.
+    """
+    if is_anchor(i, F):
+        return list(range(F))
+    return sorted(set(window_frames(chunk_of(i), F)) | {0, F - 1})
+
+
+def forward_frames(i: int, F: int) -> list[int]:
+    """Frames summarised by the forward state of query frame i, ascending:
+    all frames before its window that are not anchors."""
+    if is_anchor(i, F):
+        return []
+    first = min(window_frames(chunk_of(i), F))
+    return [j for j in range(F) if j < first and not is_anchor(j, F)]
+
+
+def backward_frames(i: int, F: int) -> list[int]:
+    """Frames summarised by the backward state of query frame i, ascending:
+    all frames after its window that are not anchors."""
+    if is_anchor(i, F):
+        return []
+    last = max(window_frames(chunk_of(i), F))
+    return [j for j in range(F) if j > last and not is_anchor(j, F)]
+
+
+def frame_mask(F: int) -> np.ndarray:
+    """Boolean [F, F]: entry (i, j) is True when query frame i attends key frame j."""
+    m = np.zeros((F, F), dtype=bool)
+    for i in range(F):
+        m[i, softmax_frames(i, F)] = True
+    return m
+
+
+# --------------------------------------------------------------------------
+# Softmax branch
+# --------------------------------------------------------------------------
+
+def _softmax_rows(s: np.ndarray) -> np.ndarray:
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    return p / p.sum(axis=-1, keepdims=True)
+
+
+def softmax_branch(q, k, v, frames=None, heads=None) -> np.ndarray:
+    """Windowed + anchored softmax attention, one query frame at a time.
+
+    Returns float64 [len(frames), N, len(heads), d] for the requested query
+    frames and heads (all by default).  q, k, v: [F, N, H, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    F, N, H, d = q.shape
+    frames = list(range(F)) if frames is None else list(frames)
+    heads = list(range(H)) if heads is None else list(heads)
+    out = np.zeros((len(frames), N, len(heads), d))
+    for a, h in enumerate(heads):
+        for b, i in enumerate(frames):
+            keys = np.concatenate([k[j, :, h, :] for j in softmax_frames(i, F)], axis=0)
+            vals = np.concatenate([v[j, :, h, :] for j in softmax_frames(i, F)], axis=0)
+            p = _softmax_rows(q[i, :, h, :] @ keys.T / math.sqrt(d))
+            out[b, :, a, :] = p @ vals
+    return out
+
+
+def softmax_branch_dense(q, k, v) -> np.ndarray:
+    """Same branch as dense attention over all F*N tokens under the explicit
+    token mask expanded from frame_mask (small inputs only)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    F, N, H, d = q.shape
+    tok_mask = np.kron(frame_mask(F), np.ones((N, N), dtype=bool)).astype(bool)
+    out = np.zeros_like(q)
+    for h in range(H):
+        Q = q[:, :, h, :].reshape(F * N, d)
+        K = k[:, :, h, :].reshape(F * N, d)
+        V = v[:, :, h, :].reshape(F * N, d)
+        s = np.where(tok_mask, Q @ K.T / math.sqrt(d), -np.inf)
+        out[:, :, h, :] = (_softmax_rows(s) @ V).reshape(F, N, d)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Video Delta Attention (linear branch)
+# --------------------------------------------------------------------------
+
+def vda_update(S, K, V, beta) -> np.ndarray:
+    """One frame's state update.
+
+    S: [dv, dk] state; K: [dk, Nt] keys of the frame as columns; V: [dv, Nt]
+    values as columns; beta: scalar.  Returns (S + beta V K^T)(I + beta K K^T)^-1,
+    the minimiser of beta * ||X K - V||^2 + ||X - S||^2.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    return vda_update_grams(S, K @ K.T, V @ K.T, beta)
+
+
+def vda_update_grams(S, G, B, beta) -> np.ndarray:
+    """vda_update given the frame's Grams G = K K^T and B = V K^T."""
+    d = G.shape[0]
+    A = np.eye(d) + beta * G            # symmetric positive definite
+    R = np.asarray(S, dtype=np.float64) + beta * B
+    # X A = R  <=>  A X^T = R^T  (A = A^T)
+    return np.linalg.solve(A, R.T).T
+
+
+def vda_states(k, v, beta, heads=None):
+    """Forward and backward states of every chunk.
+
+    For chunk c, take any non-anchor query frame i of the chunk (all of them
+    have the same window and hence the same Phi and Psi).  S_fwd[c] applies the
+    update over forward_frames(i) in ascending time, starting from zero;
+    S_bwd[c] applies it over backward_frames(i) in descending time (latest frame
+    first), starting from zero.  Chunks with no non-anchor frame keep zeros.
+
+    Returns (S_fwd, S_bwd), each float64 [C, len(heads), d, d].
+    """
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    F, N, H, d = k.shape
+    heads = list(range(H)) if heads is None else list(heads)
+    C = num_chunks(F)
+    S_fwd = np.zeros((C, len(heads), d, d))
+    S_bwd = np.zeros((C, len(heads), d, d))
+    for a, h in enumerate(heads):
+        grams = {}
+
+        def gram(t):
+            if t not in grams:
+                Kt = k[t, :, h, :].T          # [d, N]
+                Vt = v[t, :, h, :].T
+                grams[t] = (Kt @ Kt.T, Vt @ Kt.T)
+            return grams[t]
+
+        for c in range(C):
+            members = [i for i in range(F) if chunk_of(i) == c and not is_anchor(i, F)]
+            if not members:
+                continue
+            i = members[0]
+            S = np.zeros((d, d))
+            for t in forward_frames(i, F):
+                G, B = gram(t)
+                S = vda_update_grams(S, G, B, beta[t, h])
+            S_fwd[c, a] = S
+            S = np.zeros((d, d))
+            for t in reversed(backward_frames(i, F)):
+                G, B = gram(t)
+                S = vda_update_grams(S, G, B, beta[t, h])
+            S_bwd[c, a] = S
+    return S_fwd, S_bwd
+
+
+def linear_branch(q, S_fwd, S_bwd, frames=None) -> np.ndarray:
+    """o = S_fwd q + S_bwd q for every token of a non-anchor frame; 0 on anchors.
+
+    S_fwd, S_bwd: [C, Hs, d, d] for the heads present in q's head axis.
+    Returns float64 [len(frames), N, Hs, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    F, N, Hs, d = q.shape
+    frames = list(range(F)) if frames is None else list(frames)
+    out = np.zeros((len(frames), N, Hs, d))
+    for b, i in enumerate(frames):
+        if is_anchor(i, F):
+            continue
+        c = chunk_of(i)
+        for h in range(Hs):
+            x = q[i, :, h, :].T                      # [d, N]
+            out[b, :, h, :] = (S_fwd[c, h] @ x + S_bwd[c, h] @ x).T
+    return out
+
+
+def merge(O_soft, O_lin, gate) -> np.ndarray:
+    """O = O_soft + g * O_lin with g per (head, channel); gate: [Hs, d]."""
+    return np.asarray(O_soft, np.float64) + np.asarray(gate, np.float64)[None, None] * O_lin
+
+
+def hybrid(q, k, v, beta, gate, dense=False):
+    """The whole layer.  Returns (O, O_soft, O_lin), each float64 [F, N, H, d]."""
+    O_soft = softmax_branch_dense(q, k, v) if dense else softmax_branch(q, k, v)
+    S_fwd, S_bwd = vda_states(k, v, beta)
+    O_lin = linear_branch(q, S_fwd, S_bwd)
+    return merge(O_soft, O_lin, gate), O_soft, O_lin
+
+
+# --------------------------------------------------------------------------
+# fp8 (OCP E4M3, "FN": no infinities, max 448) quantiser for the fp8 softmax variant
+# --------------------------------------------------------------------------
+
+def e4m3_round(x) -> np.ndarray:
+    """Round float values to the nearest E4M3 value, ties to even, saturating at +-448.
+
+    E4M3: 1 sign, 4 exponent (bias 7) and 3 mantissa bits; normal values
+    2^(e-7) * (1 + m/8), subnormals 2^-6 * m/8.  The spacing of representable
+    values around |x| is 2^(max(floor(log2|x|), -6) - 3).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    quantum = np.exp2(e - 3.0)
+    r = np.round(a / quantum) * quantum          # np.round: ties to even
+    r = np.minimum(r, E4M3_MAX)
+    return np.sign(x) * r
+
+
+def fp8_head_scales(x) -> np.ndarray:
+    """Per-head amax of x [F, N, H, d] over all tokens and channels, float32 [H]."""
+    x = np.asarray(x, dtype=np.float32)
+    return np.max(np.abs(x), axis=(0, 1, 3)).astype(np.float32)
+
+
+def fp8_quantize(x, amax) -> np.ndarray:
+    """E4M3 codes (as float64 values) of x [F, N, H, d] with per-head amax [H]:
+    code = e4m3_round(fp32(x * fp32(448 / amax))).  The scale computation and the
+    product are float32 operations so the rounding decision is taken in the same
+    precision as the device."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.asarray(amax, dtype=np.float32)
+    inv = np.where(amax > 0, np.float32(E4M3_MAX) / np.where(amax > 0, amax, np.float32(1)),
+                   np.float32(0)).astype(np.float32)
+    scaled = (x * inv[None, None, :, None]).astype(np.float32)
+    return e4m3_round(scaled)
