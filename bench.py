@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the VDN hybrid video-to-video attention layer on one MI355X.
+
+One step = one whole layer (fp8 quantiser where used, v re-layout + frame Grams,
+per-frame Cholesky maps, state scan, readout weights, windowed + anchored softmax
+attention, anchor merge, linear readout + gated merge) over one batch of seeded
+synthetic inputs already resident in HBM.
+
+Default workload: F=90 latent frames x N=4032 tokens (48 x 84 patches), H=24,
+d=128, bf16 -- the 768p / 14.4 s shaped layer.  `--config 4` runs the F=180
+fp8-q.k variant instead.
+
+Prints ONE JSON line.  Besides the contract fields it carries
+  roofline      dominant kernel (softmax attention): algorithmic FLOP per launch
+                (4 d H N^2 P(F), P = visited frame pairs) / its mean duration from
+                HIP events recorded on the launch stream around every timed launch;
+  stages_ms     mean duration of every stage over the timed steps;
+  readout       the HBM-bound readout's algorithmic bytes and fraction of 8 TB/s;
+  cpu_baseline  the fp64 oracle timed on a bounded sample (rank 0, N=1 only) and
+                extrapolated to one layer.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "hybrid-attn layer ms + TFLOP/s & %roofline at 90 frames×4032 tok, H=24,d=128"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+CONFIGS = {
+    3: dict(F=90, N=4032, H=24, d=128, precision="bf16", workload="vdn_hybrid_attn_768p_14s"),
+    4: dict(F=180, N=4032, H=24, d=128, precision="bf16_fp8qk", workload="vdn_hybrid_attn_long_stream_fp8qk"),
+    2: dict(F=45, N=1024, H=16, d=128, precision="bf16", workload="vdn_hybrid_attn_mid"),
+}
+
+
+def frame_pairs(F):
+    import hybrid_sparse_linear_chunked_amd as vdn
+    P = 0
+    for row in vdn.schedule(F):
+        nq = int(row[1]) - int(row[0]) + 1
+        nk = sum(int(row[4 + 2 * x]) - int(row[3 + 2 * x]) + 1 for x in range(int(row[2])))
+        P += nq * nk
+    return P
+
+
+def algorithmic_work(F, N, H, d):
+    """FLOP of each part of the method (not of dense attention) and readout bytes."""
+    P = frame_pairs(F)
+    C = (F + 4) // 5
+    soft = 4.0 * d * H * N * N * P                  # Q.K^T and P.V over visited pairs
+    grams = 4.0 * d * d * N * max(F - 2, 0) * H     # K K^T and V K^T per non-anchor frame
+    scan = 2.0 * H * max(F - 11, 0) * (7.0 / 3.0) * d ** 3
+    readout = 2.0 * d * d * max(F - 2, 0) * N * H
+    ro_bytes = 3.0 * max(F - 2, 0) * N * H * d * 2 + C * H * d * d * 4
+    return dict(P=P, soft=soft, grams=grams, scan=scan, readout=readout, total=soft + grams + scan + readout,
+                readout_bytes=ro_bytes)
+
+
+def cpu_baseline(F, N, H, d, seed=0, tokens=384):
+    """Time the fp64 oracle on a bounded sample of the workload and extrapolate to
+    one layer (ms).  Sample: head 0; the softmax of `tokens` query tokens of one
+    query frame of every work class (anchor / edge chunk / next-to-edge / interior);
+    head 0's whole forward + backward state computation; one frame's readout."""
+    import numpy as np
+    import torch
+    import threadpoolctl
+    import vdn_synth
+    from oracle import vdn_oracle as orc
+
+    def gen(name):
+        out = torch.empty((F, N, 1, d), dtype=torch.bfloat16)
+        vdn_synth.tensor(name, F, N, H, d, seed=seed, heads=[0], out=out,
+                         convert=lambda b: torch.from_numpy(b).to(torch.bfloat16))
+        return out.to(torch.float64).numpy()
+
+    q, k, v = gen("q"), gen("k"), gen("v")
+    beta = vdn_synth.beta(F, H, seed=seed).astype(np.float64)[:, :1]
+    classes = {}
+    for i in range(F):
+        classes.setdefault(len(orc.softmax_frames(i, F)), []).append(i)
+    t0 = time.perf_counter()
+    soft_s = 0.0
+    for nk, frames in sorted(classes.items()):
+        i = frames[len(frames) // 2]
+        a = time.perf_counter()
+        orc.softmax_branch(q, k, v, frames=[i], heads=[0], tokens=range(tokens))
+        per_token = (time.perf_counter() - a) / tokens
+        soft_s += per_token * N * len(frames)
+    a = time.perf_counter()
+    Sf, Sb = orc.vda_states(k, v, beta)
+    states_s = time.perf_counter() - a
+    a = time.perf_counter()
+    mid = F // 2
+    orc.linear_branch(q, Sf, Sb, frames=[mid])
+    readout_s = (time.perf_counter() - a) * max(F - 2, 0)
+    sample_s = time.perf_counter() - t0
+    layer_ms = 1000.0 * H * (soft_s + states_s + readout_s)
+    info = threadpoolctl.threadpool_info()
+    cores = max([x.get("num_threads", 1) for x in info] or [1])
+    return {
+        "value": layer_ms, "unit": "ms", "cores": cores, "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle, head 0 of {H}: softmax of {tokens} query tokens of one frame "
+                   f"per work class ({len(classes)} classes), full forward+backward VDA states, one "
+                   f"frame's readout; extrapolated by token/frame counts and x{H} heads; "
+                   f"{sample_s:.1f} s of CPU work"),
+        "sample_seconds": sample_s,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3, choices=sorted(CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the layer shards by head across GPUs but no multi-GPU path is built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hybrid_sparse_linear_chunked_amd as vdn
+    import vdn_synth
+
+    cfg = CONFIGS[args.config]
+    F, N, H, d, prec = cfg["F"], cfg["N"], cfg["H"], cfg["d"], cfg["precision"]
+    p = vdn.PRECISIONS[prec]
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+
+    def gen(name):
+        out = torch.empty((F, N, H, d), dtype=torch.bfloat16)
+        vdn_synth.tensor(name, F, N, H, d, out=out,
+                         convert=lambda b: torch.from_numpy(b).to(torch.bfloat16))
+        return out.to(dev)
+
+    q, k, v = gen("q"), gen("k"), gen("v")
+    beta = torch.from_numpy(vdn_synth.beta(F, H)).to(dev)
+    gate = torch.from_numpy(vdn_synth.gate(H, d)).to(dev)
+    O = torch.empty_like(q)
+    ws = vdn.new_workspace(F, N, H, d, p, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; workspace "
+          f"{ws.numel() / 2**30:.2f} GiB", file=sys.stderr, flush=True)
+
+    def step():
+        vdn.hybrid_attn(q, k, v, beta, gate, precision=p, out=O, workspace=ws)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+
+    nst = len(vdn.STAGES)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nst)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        for st in range(nst):
+            vdn.set_stage_events(st, ev[s][st][0], ev[s][st][1])
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    for st in range(nst):
+        vdn.set_stage_events(st, None, None)
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / args.steps
+    stages = {}
+    for st, name in enumerate(vdn.STAGES):
+        vals = []
+        for s in range(args.steps):
+            try:
+                vals.append(ev[s][st][0].elapsed_time(ev[s][st][1]))
+            except RuntimeError:        # stage not run in this precision
+                pass
+        if vals:
+            stages[name] = sum(vals) / len(vals)
+    print(f"[bench] {args.steps} steps: {ms:.2f} ms/step (wall {1000 * wall / args.steps:.2f})",
+          file=sys.stderr, flush=True)
+
+    work = algorithmic_work(F, N, H, d)
+    attn_ms = stages["attn"]
+    if prec == "bf16_fp8qk":
+        # q.k at the fp8 peak, p.v at the bf16 peak: report against their time-weighted peak
+        half = work["soft"] / 2
+        peak = work["soft"] / (half / PEAK_FP8_TFLOPS + half / PEAK_BF16_TFLOPS)
+    else:
+        peak = PEAK_BF16_TFLOPS
+    achieved = work["soft"] / (attn_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": "attn_kernel", "flop_per_launch": work["soft"], "kernel_ms": round(attn_ms, 3)}
+    ro_ms = stages.get("readout")
+    readout = None
+    if ro_ms:
+        gbs = work["readout_bytes"] / (ro_ms * 1e-3) / 1e9
+        readout = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": work["readout_bytes"],
+                   "kernel_ms": round(ro_ms, 4)}
+    result = {
+        "metric": METRIC, "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg["workload"], "F": F, "N": N, "H": H, "d": d, "precision": prec,
+                   "frame_pairs": work["P"]},
+        "tflops": round(work["total"] / (ms * 1e-3) / 1e12, 2),
+        "layer_flop": work["total"],
+        "roofline": roofline,
+        "readout": readout,
+        "stages_ms": {k2: round(v2, 4) for k2, v2 in stages.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a bounded sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(F, N, H, d)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,233 @@
+"""Python binding of libvdn_hybrid_attn.so, the gfx950 Video DeltaNet hybrid
+video-to-video attention layer (see include/vdn_hybrid_attn.h for the ABI).
+
+The binding only marshals arguments: it checks devices, dtypes, shapes and
+contiguity, allocates outputs and the workspace with torch, and passes raw device
+pointers and torch's current HIP stream to the C entry points.  Every step of the
+computation runs in the library's HIP kernels; if the library is not built the
+calls raise instead of computing anything another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvdn_hybrid_attn.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+PREC_FP32, PREC_BF16, PREC_BF16_FP8QK = 0, 1, 2
+PRECISIONS = {"fp32": PREC_FP32, "bf16": PREC_BF16, "bf16_fp8qk": PREC_BF16_FP8QK}
+SCHED_COLS = 13
+STAGES = ("prep", "factor", "scan", "wprep", "attn", "combine", "readout", "quant")
+
+# C signatures: (name, restype, argtypes)
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+_SIGS = {
+    "vdn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "vdn_hybrid_attn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "vdn_softmax_branch": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "vdn_vda_states": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "vdn_vda_linear": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "vdn_fp8_quantize": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
+    "vdn_schedule": (_I, [_I, ctypes.POINTER(ctypes.c_int), _I]),
+    "vdn_set_stage_events": (_I, [_I, _P, _P]),
+    "vdn_status_string": (ctypes.c_char_p, [_I]),
+    "vdn_last_hip_error": (_I, []),
+}
+EXPORTS = tuple(_SIGS)
+
+_lib = None
+
+
+class VdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load()
+        msg = lib.vdn_status_string(status).decode()
+        if status == ERR_HIP:
+            msg += f" (hipError_t {lib.vdn_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [{status}]")
+        self.status = status
+
+
+def load(path: str | None = None):
+    """Load the shared library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m hybrid_sparse_linear_chunked_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise VdnError(status, where)
+
+
+def schedule(F: int) -> np.ndarray:
+    """Frame partition table of the layer (host only): int32 [rows, 13]."""
+    lib = load()
+    n = lib.vdn_schedule(F, None, 0)
+    if n < 0:
+        raise VdnError(n, "vdn_schedule")
+    buf = (ctypes.c_int * (n * SCHED_COLS))()
+    lib.vdn_schedule(F, buf, n)
+    return np.frombuffer(buf, dtype=np.int32).reshape(n, SCHED_COLS).copy()
+
+
+def workspace_bytes(F: int, N: int, H: int, d: int, precision: int) -> int:
+    return int(load().vdn_workspace_bytes(F, N, H, d, precision))
+
+
+# ------------------------------------------------------------------ torch side
+def _torch():
+    import torch
+    return torch
+
+
+def _precision_of(x, precision):
+    torch = _torch()
+    if precision is None:
+        return PREC_FP32 if x.dtype == torch.float32 else PREC_BF16
+    return PRECISIONS[precision] if isinstance(precision, str) else int(precision)
+
+
+def _check_io(name, x, dtype, shape=None):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if x.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {x.dtype}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(x.shape)}")
+
+
+def _io_dtype(prec):
+    torch = _torch()
+    return torch.float32 if prec == PREC_FP32 else torch.bfloat16
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _workspace(F, N, H, d, prec, device, workspace=None):
+    torch = _torch()
+    need = workspace_bytes(F, N, H, d, prec)
+    if need == 0:
+        raise VdnError(ERR_UNSUPPORTED, "vdn_workspace_bytes")
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < need:
+            raise VdnError(ERR_WORKSPACE, "workspace")
+        return workspace
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
+def new_workspace(F, N, H, d, precision, device="cuda"):
+    """A workspace tensor for repeated calls with this shape."""
+    return _workspace(F, N, H, d, precision if isinstance(precision, int) else PRECISIONS[precision], device)
+
+
+def hybrid_attn(q, k, v, beta, gate, precision=None, out=None, workspace=None):
+    """O = O_soft + g (.) O_lin for q, k, v [F, N, H, d]; beta fp32 [F, H]; gate fp32 [H, d]."""
+    torch = _torch()
+    prec = _precision_of(q, precision)
+    F, N, H, d = q.shape
+    dt = _io_dtype(prec)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_io(name, x, dt, (F, N, H, d))
+    _check_io("beta", beta, torch.float32, (F, H))
+    _check_io("gate", gate, torch.float32, (H, d))
+    O = torch.empty_like(q) if out is None else out
+    _check_io("out", O, dt, (F, N, H, d))
+    ws = _workspace(F, N, H, d, prec, q.device, workspace)
+    st = load().vdn_hybrid_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+                                gate.data_ptr(), F, N, H, d, prec, O.data_ptr(), ws.data_ptr(),
+                                ws.numel(), _stream())
+    _check(st, "vdn_hybrid_attn")
+    return O
+
+
+def softmax_branch(q, k, v, precision=None, out=None, workspace=None):
+    prec = _precision_of(q, precision)
+    F, N, H, d = q.shape
+    dt = _io_dtype(prec)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_io(name, x, dt, (F, N, H, d))
+    O = _torch().empty_like(q) if out is None else out
+    _check_io("out", O, dt, (F, N, H, d))
+    ws = _workspace(F, N, H, d, prec, q.device, workspace)
+    st = load().vdn_softmax_branch(q.data_ptr(), k.data_ptr(), v.data_ptr(), F, N, H, d, prec,
+                                   O.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
+    _check(st, "vdn_softmax_branch")
+    return O
+
+
+def vda_states(k, v, beta, precision=None, workspace=None):
+    """(S_fwd, S_bwd), each fp32 [C, H, d, d]."""
+    torch = _torch()
+    prec = _precision_of(k, precision)
+    F, N, H, d = k.shape
+    dt = _io_dtype(prec)
+    _check_io("k", k, dt, (F, N, H, d))
+    _check_io("v", v, dt, (F, N, H, d))
+    _check_io("beta", beta, torch.float32, (F, H))
+    C = (F + 4) // 5
+    Sf = torch.empty((C, H, d, d), dtype=torch.float32, device=k.device)
+    Sb = torch.empty_like(Sf)
+    ws = _workspace(F, N, H, d, prec, k.device, workspace)
+    st = load().vdn_vda_states(k.data_ptr(), v.data_ptr(), beta.data_ptr(), F, N, H, d, prec,
+                               Sf.data_ptr(), Sb.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
+    _check(st, "vdn_vda_states")
+    return Sf, Sb
+
+
+def vda_linear(q, S_fwd, S_bwd, precision=None, workspace=None):
+    """Ungated O_lin [F, N, H, d]."""
+    torch = _torch()
+    prec = _precision_of(q, precision)
+    F, N, H, d = q.shape
+    C = (F + 4) // 5
+    _check_io("q", q, _io_dtype(prec), (F, N, H, d))
+    _check_io("S_fwd", S_fwd, torch.float32, (C, H, d, d))
+    _check_io("S_bwd", S_bwd, torch.float32, (C, H, d, d))
+    O = torch.empty_like(q)
+    ws = _workspace(F, N, H, d, prec, q.device, workspace)
+    st = load().vdn_vda_linear(q.data_ptr(), S_fwd.data_ptr(), S_bwd.data_ptr(), F, N, H, d, prec,
+                               O.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
+    _check(st, "vdn_vda_linear")
+    return O
+
+
+def fp8_quantize(x):
+    """(codes uint8 [F, N, H, d], amax fp32 [H]) of a bf16 tensor."""
+    torch = _torch()
+    F, N, H, d = x.shape
+    _check_io("x", x, torch.bfloat16)
+    codes = torch.empty((F, N, H, d), dtype=torch.uint8, device=x.device)
+    amax = torch.empty((H,), dtype=torch.float32, device=x.device)
+    st = load().vdn_fp8_quantize(x.data_ptr(), F, N, H, d, codes.data_ptr(), amax.data_ptr(), _stream())
+    _check(st, "vdn_fp8_quantize")
+    return codes, amax
+
+
+def set_stage_events(stage: int, before=None, after=None):
+    """Record torch.cuda.Event pairs around a stage's kernels (None, None stops)."""
+    b = None if before is None else ctypes.c_void_p(before.cuda_event)
+    a = None if after is None else ctypes.c_void_p(after.cuda_event)
+    _check(load().vdn_set_stage_events(stage, b, a), "vdn_set_stage_events")

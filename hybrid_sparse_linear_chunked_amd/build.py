@@ -1,0 +1,46 @@
+"""Build the gfx950 shared library libvdn_hybrid_attn.so in-tree with hipcc.
+
+Usage: python -m hybrid_sparse_linear_chunked_amd.build   (or call build()).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libvdn_hybrid_attn.so")
+SOURCES = ["api.cpp", "attn.hip", "vda.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # hipcc -O3 forms packed fp32 instructions on its own; keep them off
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    "-Wno-unused-command-line-argument",
+]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 into the package directory; returns the path."""
+    srcs = []
+    for s in SOURCES:
+        p = os.path.join(CSRC, s)
+        srcs += (["-x", "hip", p] if s.endswith(".cpp") else [p])
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC] + FLAGS + srcs + ["-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building libvdn_hybrid_attn.so")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

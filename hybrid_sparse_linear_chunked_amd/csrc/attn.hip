@@ -1,0 +1,750 @@
+// Softmax branch of the VDN hybrid video-to-video attention layer (gfx950).
+//
+// What is computed (sd114.wiki article "VDN-Minimax-H3 ...", section
+// 双向滑动窗口Softmax分支): five latent frames form a chunk; the tokens of a query
+// frame of chunk c attend, with softmax(q.k / sqrt(d)), to every token of the
+// frames of chunks c-1, c, c+1 and of the first and last frame; the first and
+// last frame attend to every frame.  No causal mask.
+//
+// Kernels in this file
+//   prep_kernel      one pass over k and v per (frame, head): writes v transposed
+//                    into 64-key blocks (the P.V operand layout of attn_kernel) and,
+//                    for non-anchor frames, the frame's Grams G = K K^T and
+//                    B = V K^T in fp32 (the VDA branch's inputs) with bf16 MFMA.
+//   attn_kernel      flash-style attention: a 128-query tile against the key
+//                    frames of its chunk (or one slice of all frames for anchor
+//                    query frames), K / V^T tiles double-buffered in LDS, online
+//                    softmax in fp32 registers, 32x32 MFMA for Q.K^T and P.V.
+//   combine_kernel   log-sum-exp merge of the anchor rows' key slices.
+//   amax / quant     per-head E4M3 quantiser of the fp8 Q.K^T variant.
+#include "common.h"
+#include "kernels.h"
+
+namespace vdn {
+
+// ============================================================ layouts
+// v transposed ("vt"): bf16 [H][F][nb][D][64], nb = ceil(N / 64).  Block (h, f, b)
+// holds the values of keys f*N + 64b + (0..63) (zero past the frame's end), one
+// row of 64 keys per channel.  Inside each group of 16 keys the order is
+//   position 16u + 8g + e  <->  key 16u + 8(e/4) + 4g + e%4   (g = 0, 1; e = 0..7),
+// which is the key order in which a 32x32 MFMA output tile hands its scores to
+// the next MFMA's B operand (see attn_kernel), so each lane's eight P.V operand
+// values are 16 contiguous bytes.
+__device__ inline int vt_pos_of_key(int n) {   // n in [0, 64)
+  int u = n >> 4, r = n & 15;
+  return 16 * u + 8 * ((r & 7) >> 2) + 4 * (r >> 3) + (r & 3);
+}
+
+// ============================================================ prep (bf16)
+// grid (F, H), 512 threads.  LDS: K^T and V^T of one 64-token tile, keys permuted
+// as in the vt layout (the Gram products only need both operands in the same
+// token order).
+template <int D>
+__global__ __launch_bounds__(512) void prep_kernel(const uint16_t* __restrict__ k,
+                                                   const uint16_t* __restrict__ v, int F, int N,
+                                                   int H, uint16_t* __restrict__ vt,
+                                                   float* __restrict__ G, float* __restrict__ B,
+                                                   int do_grams) {
+  constexpr int P = 64 + 8;                      // LDS row pitch (bf16)
+  constexpr int NB = D / 32;                     // 32-channel blocks per side
+  constexpr int NBLK = 2 * NB * NB;              // G blocks then B blocks
+  constexpr int PER_WAVE = (NBLK + 7) / 8;
+  __shared__ __attribute__((aligned(16))) uint16_t KT[D * P];
+  __shared__ __attribute__((aligned(16))) uint16_t VT[D * P];
+
+  const int f = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int j = lane & 31, hf = lane >> 5;
+  const int nb = (N + 63) / 64;
+  const bool grams = do_grams && f > 0 && f < F - 1;
+  const size_t rs = (size_t)H * D;               // token stride (elements)
+
+  floatx16 acc[PER_WAVE];
+#pragma unroll
+  for (int x = 0; x < PER_WAVE; ++x) acc[x] = floatx16{};
+
+  for (int b = 0; b < nb; ++b) {
+    const int nvalid = min(64, N - 64 * b);
+    // global -> registers -> LDS (transposed, permuted keys)
+    constexpr int CH = 64 * D / 8;               // 16-byte chunks per tensor tile
+    for (int c = tid; c < 2 * CH; c += 512) {
+      const bool isv = c >= CH;
+      const int cc = isv ? c - CH : c;
+      const int n = cc / (D / 8), c8 = cc % (D / 8);
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (n < nvalid) {
+        const uint16_t* src = (isv ? v : k) + ((size_t)f * N + 64 * b + n) * rs + (size_t)h * D + 8 * c8;
+        val = *reinterpret_cast<const uint4*>(src);
+      }
+      uint16_t* T = isv ? VT : KT;
+      const int p = vt_pos_of_key(n);
+      const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        T[(8 * c8 + e) * P + p] = static_cast<uint16_t>(wv[e >> 1] >> (16 * (e & 1)));
+    }
+    __syncthreads();
+    // V^T block out: D rows x 64 keys
+    {
+      uint16_t* dst = vt + (((size_t)h * F + f) * nb + b) * (size_t)(D * 64);
+      for (int c = tid; c < D * 8; c += 512) {
+        const int row = c >> 3, c8 = c & 7;
+        *reinterpret_cast<uint4*>(dst + row * 64 + 8 * c8) =
+            *reinterpret_cast<const uint4*>(&VT[row * P + 8 * c8]);
+      }
+    }
+    if (grams) {
+#pragma unroll
+      for (int x = 0; x < PER_WAVE; ++x) {
+        const int blk = w * PER_WAVE + x;
+        if (blk < NBLK) {
+          const bool isB = blk >= NB * NB;
+          const int bb = isB ? blk - NB * NB : blk;
+          const int bi = bb / NB, bj = bb % NB;
+          const uint16_t* A = isB ? VT : KT;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            bf16x8 a = *reinterpret_cast<const bf16x8*>(&A[(32 * bi + j) * P + 16 * u + 8 * hf]);
+            bf16x8 bo = *reinterpret_cast<const bf16x8*>(&KT[(32 * bj + j) * P + 16 * u + 8 * hf]);
+            acc[x] = mfma_bf16(a, bo, acc[x]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (grams) {
+#pragma unroll
+    for (int x = 0; x < PER_WAVE; ++x) {
+      const int blk = w * PER_WAVE + x;
+      if (blk < NBLK) {
+        const bool isB = blk >= NB * NB;
+        const int bb = isB ? blk - NB * NB : blk;
+        const int bi = bb / NB, bj = bb % NB;
+        float* dst = (isB ? B : G) + ((size_t)f * H + h) * D * D;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * bi + 8 * (r >> 2) + 4 * hf + (r & 3);
+          dst[row * D + 32 * bj + j] = acc[x][r];
+        }
+      }
+    }
+  }
+}
+
+// ============================================================ attention
+// Work items, one per 128-query tile:
+//   anchor items (first and last frame, all key frames split into `nsplit`
+//   slices of `fs` frames; partial results go to part_O / part_ml), then
+//   chunk items (head-major, chunk-major: the non-anchor query frames of each
+//   chunk, as one contiguous token range, against the chunk's key frames).
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;          // fp32 path: raw v
+  const uint16_t* vt;     // bf16 / fp8 paths: transposed v
+  const uint8_t* q8;      // fp8 path: E4M3 codes
+  const uint8_t* k8;
+  const float* amax;      // fp8 path: [2][H] (q then k)
+  void* O;
+  float* part_O;          // [nsplit][H][na][N][D]
+  float* part_ml;         // [nsplit][H][na][N][2]
+  int F, N, H;
+  int nsplit, fs, na, qt_anchor;
+  int n_anchor_items;
+  int tiles_per_head;     // sum over chunks of the chunk items' tile counts
+  float scale_log2;       // log2(e) / sqrt(D)
+};
+
+constexpr int BQ = 128;   // queries per work item (4 waves x 32)
+constexpr int BK = 64;    // keys per tile
+
+template <int D, int PREC>
+struct AttnCfg {
+  static constexpr bool F32 = PREC == 0;
+  static constexpr bool FP8 = PREC == 2;
+  // K tile pitch in elements of the K operand type
+  static constexpr int KP = F32 ? D + 1 : (FP8 ? D + 16 : D + 8);
+  static constexpr int K_BYTES = F32 ? BK * KP * 4 : (FP8 ? BK * KP : BK * KP * 2);
+  // V tile: fp32 path [64 keys][D+1] floats; otherwise V^T [D][64+8] bf16
+  static constexpr int VP = F32 ? D + 1 : BK + 8;
+  static constexpr int V_BYTES = F32 ? BK * VP * 4 : D * VP * 2;
+  static constexpr int STAGE = ((K_BYTES + V_BYTES) + 15) / 16 * 16;
+  // 16-byte chunks of one tile in global memory
+  static constexpr int K_CHUNKS = F32 ? BK * D / 4 : (FP8 ? BK * D / 16 : BK * D / 8);
+  static constexpr int V_CHUNKS = F32 ? BK * D / 4 : D * BK / 8;
+  static constexpr int K_PER_T = (K_CHUNKS + 255) / 256;
+  static constexpr int V_PER_T = (V_CHUNKS + 255) / 256;
+  static constexpr int QSTEPS = F32 ? D / 2 : (FP8 ? D / 64 : D / 16);
+};
+
+// Frame of slot `s` in the key-frame list of a chunk item: the first frame (if not
+// in the window), the window frames, the last frame (if not in the window).
+__device__ inline int chunk_key_frame(int s, int wf, int we, int F) {
+  if (wf > 0) {
+    if (s == 0) return 0;
+    --s;
+  }
+  if (s < we - wf) return wf + s;
+  return F - 1;
+}
+
+template <int D, int PREC>
+__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
+  using Cfg = AttnCfg<D, PREC>;
+  constexpr bool F32 = Cfg::F32, FP8 = Cfg::FP8;
+  constexpr int NDB = D / 32;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int j = lane & 31, hf = lane >> 5;
+  const int F = a.F, N = a.N, H = a.H;
+  const size_t rs = (size_t)H * D;
+  const int nb = (N + BK - 1) / BK;
+
+  // ---------------- decode the work item
+  int h, q_tok0, q_rows, split = -1, anchor_idx = 0;
+  int kf_mode;          // 0: contiguous frames [k_f0, k_f1); 1: chunk key list
+  int k_f0 = 0, k_f1 = 0, wf = 0, we = 0, nslots;
+  int bid = blockIdx.x;
+  if (bid < a.n_anchor_items) {
+    split = bid % a.nsplit;
+    int r = bid / a.nsplit;
+    const int qt = r % a.qt_anchor;
+    r /= a.qt_anchor;
+    anchor_idx = r % a.na;
+    h = r / a.na;
+    const int qf = anchor_idx == 0 ? 0 : F - 1;
+    q_tok0 = qf * N + qt * BQ;
+    q_rows = min(BQ, N - qt * BQ);
+    kf_mode = 0;
+    k_f0 = split * a.fs;
+    k_f1 = min(F, k_f0 + a.fs);
+    nslots = k_f1 - k_f0;
+  } else {
+    int r = bid - a.n_anchor_items;
+    h = r / a.tiles_per_head;
+    r -= h * a.tiles_per_head;
+    const int C = num_chunks(F);
+    int c = 0;
+    for (; c < C; ++c) {
+      const int nf = nq_end(c, F) - nq_first(c);
+      const int t = nf > 0 ? (nf * N + BQ - 1) / BQ : 0;
+      if (r < t) break;
+      r -= t;
+    }
+    const int tok_begin = nq_first(c) * N, tok_end = nq_end(c, F) * N;
+    q_tok0 = tok_begin + r * BQ;
+    q_rows = min(BQ, tok_end - q_tok0);
+    kf_mode = 1;
+    wf = win_first(c);
+    we = win_end(c, F);
+    nslots = (wf > 0 ? 1 : 0) + (we - wf) + (we < F ? 1 : 0);
+  }
+  const int ntiles = nslots * nb;
+
+  // ---------------- Q operand fragments (B operand of S^T = K Q^T), resident
+  const int qi = 32 * w + j;                    // query row within the tile
+  const bool qvalid = qi < q_rows;
+  const size_t qoff = (size_t)(q_tok0 + qi) * rs + (size_t)h * D;
+  bf16x8 qb[F32 || FP8 ? 1 : Cfg::QSTEPS];
+  float qf[F32 ? Cfg::QSTEPS : 1];
+  intx8 q8f[FP8 ? Cfg::QSTEPS : 1];
+  if constexpr (F32) {
+    const float* q = static_cast<const float*>(a.q);
+#pragma unroll
+    for (int s = 0; s < Cfg::QSTEPS; ++s) qf[s] = qvalid ? q[qoff + 2 * s + hf] : 0.f;
+  } else if constexpr (FP8) {
+#pragma unroll
+    for (int s = 0; s < Cfg::QSTEPS; ++s) {
+      if (qvalid) {
+        const uint4* p = reinterpret_cast<const uint4*>(a.q8 + qoff + 64 * s + 32 * hf);
+        uint4 x0 = p[0], x1 = p[1];
+        q8f[s] = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      } else {
+        q8f[s] = intx8{};
+      }
+    }
+  } else {
+    const uint16_t* q = static_cast<const uint16_t*>(a.q);
+#pragma unroll
+    for (int s = 0; s < Cfg::QSTEPS; ++s)
+      qb[s] = qvalid ? *reinterpret_cast<const bf16x8*>(q + qoff + 16 * s + 8 * hf) : bf16x8{};
+  }
+  float scale = a.scale_log2;
+  if constexpr (FP8) scale *= (a.amax[h] * (1.f / 448.f)) * (a.amax[H + h] * (1.f / 448.f));
+
+  // ---------------- tile loader
+  auto tile_frame = [&](int t, int& f, int& b) {
+    const int s = t / nb;
+    b = t - s * nb;
+    f = kf_mode == 0 ? k_f0 + s : chunk_key_frame(s, wf, we, F);
+  };
+  uint4 kreg[Cfg::K_PER_T];
+  uint4 vreg[Cfg::V_PER_T];
+  auto load_tile = [&](int t) {
+    int f, b;
+    tile_frame(t, f, b);
+    const int nvalid = min(BK, N - BK * b);
+    const size_t tok0 = (size_t)f * N + BK * b;
+#pragma unroll
+    for (int x = 0; x < Cfg::K_PER_T; ++x) {
+      const int c = tid + 256 * x;
+      kreg[x] = make_uint4(0, 0, 0, 0);
+      if (c < Cfg::K_CHUNKS) {
+        constexpr int CPR = Cfg::K_CHUNKS / BK;   // chunks per key row
+        const int n = c / CPR, cc = c % CPR;
+        if (n < nvalid) {
+          if constexpr (F32)
+            kreg[x] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.k) + (tok0 + n) * rs + (size_t)h * D + 4 * cc);
+          else if constexpr (FP8)
+            kreg[x] = *reinterpret_cast<const uint4*>(a.k8 + (tok0 + n) * rs + (size_t)h * D + 16 * cc);
+          else
+            kreg[x] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + (tok0 + n) * rs + (size_t)h * D + 8 * cc);
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < Cfg::V_PER_T; ++x) {
+      const int c = tid + 256 * x;
+      vreg[x] = make_uint4(0, 0, 0, 0);
+      if (c < Cfg::V_CHUNKS) {
+        if constexpr (F32) {
+          constexpr int CPR = D / 4;
+          const int n = c / CPR, cc = c % CPR;
+          if (n < nvalid)
+            vreg[x] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.v) + (tok0 + n) * rs + (size_t)h * D + 4 * cc);
+        } else {
+          const uint16_t* src = a.vt + (((size_t)h * F + f) * nb + b) * (size_t)(D * BK);
+          vreg[x] = *reinterpret_cast<const uint4*>(src + 8 * c);
+        }
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+    unsigned char* base = smem + stage * Cfg::STAGE;
+#pragma unroll
+    for (int x = 0; x < Cfg::K_PER_T; ++x) {
+      const int c = tid + 256 * x;
+      if (c < Cfg::K_CHUNKS) {
+        constexpr int CPR = Cfg::K_CHUNKS / BK;
+        const int n = c / CPR, cc = c % CPR;
+        if constexpr (F32) {
+          float* Ks = reinterpret_cast<float*>(base);
+          Ks[n * Cfg::KP + 4 * cc + 0] = __uint_as_float(kreg[x].x);
+          Ks[n * Cfg::KP + 4 * cc + 1] = __uint_as_float(kreg[x].y);
+          Ks[n * Cfg::KP + 4 * cc + 2] = __uint_as_float(kreg[x].z);
+          Ks[n * Cfg::KP + 4 * cc + 3] = __uint_as_float(kreg[x].w);
+        } else if constexpr (FP8) {
+          *reinterpret_cast<uint4*>(base + n * Cfg::KP + 16 * cc) = kreg[x];
+        } else {
+          *reinterpret_cast<uint4*>(base + 2 * (n * Cfg::KP + 8 * cc)) = kreg[x];
+        }
+      }
+    }
+    unsigned char* vb = base + Cfg::K_BYTES;
+#pragma unroll
+    for (int x = 0; x < Cfg::V_PER_T; ++x) {
+      const int c = tid + 256 * x;
+      if (c < Cfg::V_CHUNKS) {
+        if constexpr (F32) {
+          constexpr int CPR = D / 4;
+          const int n = c / CPR, cc = c % CPR;
+          float* Vs = reinterpret_cast<float*>(vb);
+          Vs[n * Cfg::VP + 4 * cc + 0] = __uint_as_float(vreg[x].x);
+          Vs[n * Cfg::VP + 4 * cc + 1] = __uint_as_float(vreg[x].y);
+          Vs[n * Cfg::VP + 4 * cc + 2] = __uint_as_float(vreg[x].z);
+          Vs[n * Cfg::VP + 4 * cc + 3] = __uint_as_float(vreg[x].w);
+        } else {
+          const int row = c >> 3, c8 = c & 7;
+          *reinterpret_cast<uint4*>(vb + 2 * (row * Cfg::VP + 8 * c8)) = vreg[x];
+        }
+      }
+    }
+  };
+
+  // ---------------- running softmax state (per lane: query j; both halves agree on m)
+  floatx16 o[NDB];
+#pragma unroll
+  for (int x = 0; x < NDB; ++x) o[x] = floatx16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int stage = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+    const unsigned char* base = smem + stage * Cfg::STAGE;
+    int nvalid;
+    {
+      int f, b;
+      tile_frame(t, f, b);
+      nvalid = min(BK, N - BK * b);
+    }
+
+    // S^T = K Q^T for two 32-key blocks
+    floatx16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = floatx16{};
+      const int krow = 32 * kb + j;
+      if constexpr (F32) {
+        const float* Ks = reinterpret_cast<const float*>(base);
+#pragma unroll
+        for (int st = 0; st < Cfg::QSTEPS; ++st)
+          s[kb] = mfma_f32(Ks[krow * Cfg::KP + 2 * st + hf], qf[st], s[kb]);
+      } else if constexpr (FP8) {
+#pragma unroll
+        for (int st = 0; st < Cfg::QSTEPS; ++st) {
+          const uint4* p = reinterpret_cast<const uint4*>(base + krow * Cfg::KP + 64 * st + 32 * hf);
+          uint4 x0 = p[0], x1 = p[1];
+          intx8 ka = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+          s[kb] = mfma_fp8(ka, q8f[st], s[kb]);
+        }
+      } else {
+        const uint16_t* Ks = reinterpret_cast<const uint16_t*>(base);
+#pragma unroll
+        for (int st = 0; st < Cfg::QSTEPS; ++st) {
+          bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[krow * Cfg::KP + 16 * st + 8 * hf]);
+          s[kb] = mfma_bf16(ka, qb[st], s[kb]);
+        }
+      }
+    }
+    // mask keys past the frame's end; scale to log2 units
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+        float x = s[kb][r] * scale;
+        if (nvalid < BK && key >= nvalid) x = -INFINITY;
+        s[kb][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(s[kb][r] - m_new);
+        s[kb][r] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int x = 0; x < NDB; ++x) o[x] *= alpha;
+
+    // O^T += V^T P^T
+    if constexpr (F32) {
+      const float* Vs = reinterpret_cast<const float*>(base + Cfg::K_BYTES);
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int kb = u >> 4, r = u & 15;
+        const int key = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          o[db] = mfma_f32(Vs[key * Cfg::VP + 32 * db + j], s[kb][r], o[db]);
+      }
+    } else {
+      const uint16_t* Vs = reinterpret_cast<const uint16_t*>(base + Cfg::K_BYTES);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kb = u >> 1, e0 = 8 * (u & 1);
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[kb][e0 + e];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[(32 * db + j) * Cfg::VP + 16 * u + 8 * hf]);
+          o[db] = mfma_bf16(va, pb, o[db]);
+        }
+      }
+    }
+
+    if (t + 1 < ntiles) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---------------- epilogue
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!qvalid) return;
+  if (split < 0) {
+    const float inv = 1.f / l_tot;
+    const size_t ooff = (size_t)(q_tok0 + qi) * rs + (size_t)h * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * db + 8 * g + 4 * hf;
+        const float x0 = o[db][4 * g + 0] * inv, x1 = o[db][4 * g + 1] * inv;
+        const float x2 = o[db][4 * g + 2] * inv, x3 = o[db][4 * g + 3] * inv;
+        if constexpr (F32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.O) + ooff + dd) = make_float4(x0, x1, x2, x3);
+        } else {
+          uint2 pk = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.O) + ooff + dd) = pk;
+        }
+      }
+  } else {
+    const int n = q_tok0 - (anchor_idx == 0 ? 0 : (F - 1) * N) + qi;
+    const size_t row = (((size_t)split * H + h) * a.na + anchor_idx) * N + n;
+    float* po = a.part_O + row * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * db + 8 * g + 4 * hf;
+        *reinterpret_cast<float4*>(po + dd) =
+            make_float4(o[db][4 * g + 0], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+      }
+    if (hf == 0) {
+      a.part_ml[2 * row + 0] = m_run;
+      a.part_ml[2 * row + 1] = l_tot;
+    }
+  }
+}
+
+// ============================================================ combine
+// One thread per (split-merged row, 4 channels).  Rows: [H][na][N].
+template <int D, bool F32OUT>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_O,
+                                                      const float* __restrict__ part_ml, int F,
+                                                      int N, int H, int na, int nsplit, void* O) {
+  const size_t rows = (size_t)H * na * N;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * (D / 4)) return;
+  const size_t row = idx / (D / 4);
+  const int c4 = idx % (D / 4);
+  const int n = row % N;
+  const int ai = (row / N) % na;
+  const int h = row / ((size_t)N * na);
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_ml[2 * (s * rows + row)]);
+  float l = 0.f;
+  float4 acc = make_float4(0, 0, 0, 0);
+  for (int s = 0; s < nsplit; ++s) {
+    const size_t r = s * rows + row;
+    const float wgt = __builtin_amdgcn_exp2f(part_ml[2 * r] - m);
+    l += wgt * part_ml[2 * r + 1];
+    const float4 x = *reinterpret_cast<const float4*>(part_O + r * D + 4 * c4);
+    acc.x += wgt * x.x;
+    acc.y += wgt * x.y;
+    acc.z += wgt * x.z;
+    acc.w += wgt * x.w;
+  }
+  const float inv = 1.f / l;
+  const int qf = ai == 0 ? 0 : F - 1;
+  const size_t off = ((size_t)qf * N + n) * H * D + (size_t)h * D + 4 * c4;
+  if constexpr (F32OUT) {
+    *reinterpret_cast<float4*>(static_cast<float*>(O) + off) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  } else {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(O) + off) =
+        make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+  }
+}
+
+// ============================================================ fp8 quantiser
+// E4M3 ("FN": no infinities, max 448), round to nearest even, saturating.
+__device__ inline uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (!(a < 448.f)) {
+    code = 0x7Eu;                                   // +-448
+  } else if (a < 0.015625f) {                       // below 2^-6: spacing 2^-9
+    code = static_cast<uint32_t>(__builtin_rintf(a * 512.f));   // 0..8 (8 = 2^-6)
+  } else {
+    const int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xFF) - 127;   // -6..8
+    const float m = __builtin_rintf(a * __builtin_ldexpf(1.f, 3 - e));         // 8..16
+    code = static_cast<uint32_t>((e + 7) * 8 + static_cast<int>(m) - 8);
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return sign | code;
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, int n, uint32_t value) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = value;
+}
+
+// grid (ceil(F*N / 1024), H), 256 threads: max |x| over 1024 tokens of head h.
+template <int D>
+__global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, size_t ntok, int H,
+                                                   uint32_t* __restrict__ amax_bits) {
+  constexpr int CPR = D / 8;                       // 16-byte chunks per (token, head) row
+  const int h = blockIdx.y;
+  const size_t t0 = (size_t)blockIdx.x * 1024;
+  float m = 0.f;
+  for (int c = threadIdx.x; c < 1024 * CPR; c += 256) {
+    const size_t t = t0 + c / CPR;
+    if (t < ntok) {
+      const uint4 val = *reinterpret_cast<const uint4*>(x + t * H * D + (size_t)h * D + 8 * (c % CPR));
+      const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        m = fmaxf(m, fabsf(__uint_as_float(wv[e] << 16)));
+        m = fmaxf(m, fabsf(__uint_as_float(wv[e] & 0xffff0000u)));
+      }
+    }
+  }
+  m = wave_max(m);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    // non-negative floats order like their bit patterns: the max is exact and
+    // independent of the order in which blocks arrive
+    atomicMax(&amax_bits[h], __float_as_uint(m));
+  }
+}
+
+// 8 elements per thread.
+template <int D>
+__global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__ x, size_t n8, int H,
+                                                    const float* __restrict__ amax,
+                                                    uint8_t* __restrict__ codes) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const int h = static_cast<int>((i / (D / 8)) % H);
+  const float am = amax[h];
+  const float inv = am > 0.f ? 448.f / am : 0.f;
+  const uint4 val = *reinterpret_cast<const uint4*>(x + 8 * i);
+  const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
+  uint32_t out[2] = {0, 0};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t bits = (e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16);
+    const uint32_t c = f32_to_e4m3(__uint_as_float(bits) * inv);
+    out[e >> 2] |= c << (8 * (e & 3));
+  }
+  *reinterpret_cast<uint2*>(codes + 8 * i) = make_uint2(out[0], out[1]);
+}
+
+// ============================================================ launchers
+template <int D>
+static hipError_t prep_d(const uint16_t* k, const uint16_t* v, int F, int N, int H, uint16_t* vt,
+                         float* G, float* B, int grams, hipStream_t st) {
+  hipLaunchKernelGGL(prep_kernel<D>, dim3(F, H), dim3(512), 0, st, k, v, F, N, H, vt, G, B, grams);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const uint16_t* k, const uint16_t* v, int F, int N, int H, int D,
+                       uint16_t* vt, float* G, float* B, int grams, hipStream_t st) {
+  switch (D) {
+    case 32: return prep_d<32>(k, v, F, N, H, vt, G, B, grams, st);
+    case 64: return prep_d<64>(k, v, F, N, H, vt, G, B, grams, st);
+    case 128: return prep_d<128>(k, v, F, N, H, vt, G, B, grams, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+void attn_split_plan(int F, int* nsplit, int* fs) {
+  // anchor query frames see all F key frames; slice them into pieces of about
+  // the length of an interior chunk's key list (17 frames) for load balance
+  int ns = (F + 14) / 15;
+  if (ns < 1) ns = 1;
+  int f = (F + ns - 1) / ns;
+  *fs = f;
+  *nsplit = (F + f - 1) / f;
+}
+
+template <int D, int PREC>
+static hipError_t attn_d(AttnArgs a, hipStream_t st) {
+  using Cfg = AttnCfg<D, PREC>;
+  const int lds = 2 * Cfg::STAGE;
+  static bool attr_done = false;     // benign race: the attribute value is the same
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<D, PREC>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  const int nitems = a.n_anchor_items + a.H * a.tiles_per_head;
+  if (nitems == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_kernel<D, PREC>), dim3(nitems), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, const uint16_t* vt,
+                       const uint8_t* q8, const uint8_t* k8, const float* amax, int F, int N, int H,
+                       int D, void* O, float* part_O, float* part_ml, hipStream_t st) {
+  AttnArgs a;
+  a.q = q; a.k = k; a.v = v; a.vt = vt; a.q8 = q8; a.k8 = k8; a.amax = amax;
+  a.O = O; a.part_O = part_O; a.part_ml = part_ml;
+  a.F = F; a.N = N; a.H = H;
+  attn_split_plan(F, &a.nsplit, &a.fs);
+  a.na = F >= 2 ? 2 : 1;
+  a.qt_anchor = (N + BQ - 1) / BQ;
+  a.n_anchor_items = H * a.na * a.qt_anchor * a.nsplit;
+  int tph = 0;
+  for (int c = 0; c < num_chunks(F); ++c) {
+    const int nf = nq_end(c, F) - nq_first(c);
+    if (nf > 0) tph += (int)(((long long)nf * N + BQ - 1) / BQ);
+  }
+  a.tiles_per_head = tph;
+  a.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+#define VDN_ATTN_CASE(DD, PP) \
+  if (D == DD && prec == PP) return attn_d<DD, PP>(a, st);
+  VDN_ATTN_CASE(32, 0) VDN_ATTN_CASE(64, 0) VDN_ATTN_CASE(128, 0)
+  VDN_ATTN_CASE(32, 1) VDN_ATTN_CASE(64, 1) VDN_ATTN_CASE(128, 1)
+  VDN_ATTN_CASE(64, 2) VDN_ATTN_CASE(128, 2)
+#undef VDN_ATTN_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_combine(int prec, const float* part_O, const float* part_ml, int F, int N, int H,
+                          int D, void* O, hipStream_t st) {
+  int nsplit, fs;
+  attn_split_plan(F, &nsplit, &fs);
+  const int na = F >= 2 ? 2 : 1;
+  const size_t threads = (size_t)H * na * N * (D / 4);
+  const dim3 grid((unsigned)((threads + 255) / 256));
+#define VDN_COMB(DD)                                                                                   \
+  if (D == DD) {                                                                                       \
+    if (prec == 0)                                                                                     \
+      hipLaunchKernelGGL((combine_kernel<DD, true>), grid, dim3(256), 0, st, part_O, part_ml, F, N, H, \
+                         na, nsplit, O);                                                               \
+    else                                                                                               \
+      hipLaunchKernelGGL((combine_kernel<DD, false>), grid, dim3(256), 0, st, part_O, part_ml, F, N,   \
+                         H, na, nsplit, O);                                                            \
+    return hipGetLastError();                                                                          \
+  }
+  VDN_COMB(32) VDN_COMB(64) VDN_COMB(128)
+#undef VDN_COMB
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fp8_quant(const uint16_t* x, int F, int N, int H, int D, uint8_t* codes,
+                            float* amax, hipStream_t st) {
+  const size_t ntok = (size_t)F * N;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((H + 255) / 256), dim3(256), 0, st,
+                     reinterpret_cast<uint32_t*>(amax), H, 0u);
+  const dim3 g1((unsigned)((ntok + 1023) / 1024), H);
+  const size_t n8 = ntok * H * D / 8;
+  const dim3 g2((unsigned)((n8 + 255) / 256));
+  switch (D) {
+    case 64:
+      hipLaunchKernelGGL(amax_kernel<64>, g1, dim3(256), 0, st, x, ntok, H, reinterpret_cast<uint32_t*>(amax));
+      hipLaunchKernelGGL(quant_kernel<64>, g2, dim3(256), 0, st, x, n8, H, amax, codes);
+      break;
+    case 128:
+      hipLaunchKernelGGL(amax_kernel<128>, g1, dim3(256), 0, st, x, ntok, H, reinterpret_cast<uint32_t*>(amax));
+      hipLaunchKernelGGL(quant_kernel<128>, g2, dim3(256), 0, st, x, n8, H, amax, codes);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vdn

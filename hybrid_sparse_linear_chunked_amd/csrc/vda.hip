@@ -1,0 +1,561 @@
+// Video Delta Attention (VDA) branch of the VDN hybrid layer (gfx950).
+//
+// The memory is updated once per frame, all of the frame's tokens jointly solving
+// one update that is non-expansive (besthub article "VDN-H3 Generates 14-Second
+// 768p Video ...", section Video Delta Attention (VDA)).  Form implemented:
+//     S_t = (S_{t-1} + beta_t B_t) A_t^-1,  A_t = I + beta_t G_t,
+//     G_t = K_t K_t^T,  B_t = V_t K_t^T   (K_t, V_t: d x N, the frame's tokens).
+// Both directions apply the same per-frame affine map S -> S M_t + C_t with
+// M_t = A_t^-1 and C_t = beta_t B_t M_t, so the maps are built for every frame in
+// parallel (factor_kernel) and the serial part (scan_kernel) is one small GEMM
+// per frame.  The forward state of chunk c is the state after frames 1..5c-6
+// (ascending), the backward state the state after frames F-2 down to 5(c+2)
+// (sd114.wiki article "VDN-Minimax-H3 ...", section 双向线性注意力分支: the states
+// cover the frames before / after the window and never the window or anchors).
+// The readout adds g (.) ((S_fwd + S_bwd) q) to the softmax output.
+#include "common.h"
+#include "kernels.h"
+
+namespace vdn {
+
+// ============================================================ Grams (fp32 path)
+// grid (F, H), 256 threads; G = K^T K and B = V^T K over the frame's tokens
+// (K, V: N x D token-major), frames 1..F-2 only.
+template <int D>
+__global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__ k,
+                                                       const float* __restrict__ v, int F, int N,
+                                                       int H, float* __restrict__ G,
+                                                       float* __restrict__ B) {
+  const int f = blockIdx.x, h = blockIdx.y;
+  if (f == 0 || f == F - 1) return;
+  constexpr int TN = 16;
+  constexpr int PER = 4;                          // entries per thread per pass
+  __shared__ float Ks[TN][D], Vs[TN][D];
+  const size_t rs = (size_t)H * D;
+  const size_t base = ((size_t)f * H + h) * D * D;
+  for (int e0 = 0; e0 < D * D; e0 += 256 * PER) {
+    float g[PER], bb[PER];
+#pragma unroll
+    for (int x = 0; x < PER; ++x) g[x] = bb[x] = 0.f;
+    for (int n0 = 0; n0 < N; n0 += TN) {
+      __syncthreads();
+      for (int c = threadIdx.x; c < TN * D; c += 256) {
+        const int n = c / D, ch = c % D;
+        const bool ok = n0 + n < N;
+        const size_t off = ((size_t)f * N + n0 + n) * rs + (size_t)h * D + ch;
+        Ks[n][ch] = ok ? k[off] : 0.f;
+        Vs[n][ch] = ok ? v[off] : 0.f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int x = 0; x < PER; ++x) {
+        const int e = e0 + threadIdx.x + 256 * x;
+        if (e < D * D) {
+          const int r = e / D, c = e % D;
+          for (int n = 0; n < TN; ++n) {
+            g[x] += Ks[n][r] * Ks[n][c];
+            bb[x] += Vs[n][r] * Ks[n][c];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int e = e0 + threadIdx.x + 256 * x;
+      if (e < D * D) {
+        G[base + e] = g[x];
+        B[base + e] = bb[x];
+      }
+    }
+  }
+}
+
+// ============================================================ per-frame affine maps
+// grid (F-2, H), 256 threads; frame t = blockIdx.x + 1.
+// In:  G = K K^T, B = V K^T of frame t.   Out (in place): G <- M = A^-1,
+// B <- C = beta B M, with A = I + beta G.
+//   1. Cholesky A = L L^T, right-looking: the matrix lives in registers (thread
+//      (ty, tx) of a 16 x 16 grid owns an RB x RB block), the pivot column is
+//      broadcast through LDS, one barrier per column.
+//   2. Y = L^-1 by forward substitution on the identity, same layout, pivot row
+//      broadcast through LDS.
+//   3. M = Y^T Y and C = beta B M with fp32 MFMA (32x32x2) from LDS.
+template <int D>
+__global__ __launch_bounds__(256) void factor_kernel(float* __restrict__ G, float* __restrict__ Bm,
+                                                     const float* __restrict__ beta, int F, int H) {
+  constexpr int RB = D / 16;
+  constexpr int LP = D + 1;
+  constexpr int NB = D / 32;
+  constexpr int NBLK = NB * NB;
+  constexpr int PER_WAVE = (NBLK + 3) / 4;
+  extern __shared__ float sm[];
+  float* Ls = sm;                 // [D][LP]: L, later M
+  float* Xs = sm + D * LP;        // [D][LP]: Y, later B
+  float* cbuf = Xs + D * LP;      // [2][D]
+
+  const int t = blockIdx.x + 1, h = blockIdx.y;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int lane = tid & 63, w = tid >> 6, j = lane & 31, hf = lane >> 5;
+  const float b = beta[(size_t)t * H + h];
+  float* Gp = G + ((size_t)t * H + h) * D * D;
+  float* Bp = Bm + ((size_t)t * H + h) * D * D;
+
+  float a[RB][RB];
+#pragma unroll
+  for (int ii = 0; ii < RB; ++ii)
+#pragma unroll
+    for (int kk = 0; kk < RB; ++kk) {
+      const int r = ty * RB + ii, c = tx * RB + kk;
+      a[ii][kk] = b * Gp[r * D + c] + (r == c ? 1.f : 0.f);
+    }
+
+  // ---- 1. Cholesky
+  for (int jb = 0; jb < 16; ++jb) {
+#pragma unroll
+    for (int jr = 0; jr < RB; ++jr) {
+      const int jj = jb * RB + jr;
+      float* cb = cbuf + (jj & 1) * D;
+      if (tx == jb) {
+#pragma unroll
+        for (int ii = 0; ii < RB; ++ii) cb[ty * RB + ii] = a[ii][jr];
+      }
+      __syncthreads();
+      const float dj = cb[jj];
+      const float rsq = 1.f / sqrtf(dj);
+      const float inv_d = 1.f / dj;
+      if (tx == jb) {
+#pragma unroll
+        for (int ii = 0; ii < RB; ++ii) {
+          const int i = ty * RB + ii;
+          Ls[i * LP + jj] = i >= jj ? cb[i] * rsq : 0.f;
+        }
+      }
+      float cr[RB], cc[RB];
+#pragma unroll
+      for (int x = 0; x < RB; ++x) {
+        cr[x] = cb[ty * RB + x];
+        cc[x] = cb[tx * RB + x];
+      }
+#pragma unroll
+      for (int ii = 0; ii < RB; ++ii)
+#pragma unroll
+        for (int kk = 0; kk < RB; ++kk) {
+          const int r = ty * RB + ii, c = tx * RB + kk;
+          if (r > jj && c > jj) a[ii][kk] -= cr[ii] * cc[kk] * inv_d;
+        }
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. Y = L^-1 (reuse a[][] as Y)
+#pragma unroll
+  for (int ii = 0; ii < RB; ++ii)
+#pragma unroll
+    for (int kk = 0; kk < RB; ++kk) a[ii][kk] = (ty * RB + ii == tx * RB + kk) ? 1.f : 0.f;
+  for (int kb = 0; kb < 16; ++kb) {
+#pragma unroll
+    for (int kr = 0; kr < RB; ++kr) {
+      const int k = kb * RB + kr;
+      float* rb = cbuf + (k & 1) * D;
+      if (ty == kb) {
+        const float inv = 1.f / Ls[k * LP + k];
+#pragma unroll
+        for (int kk = 0; kk < RB; ++kk) {
+          a[kr][kk] *= inv;
+          rb[tx * RB + kk] = a[kr][kk];
+        }
+      }
+      __syncthreads();
+      float rv[RB];
+#pragma unroll
+      for (int kk = 0; kk < RB; ++kk) rv[kk] = rb[tx * RB + kk];
+#pragma unroll
+      for (int ii = 0; ii < RB; ++ii) {
+        const int r = ty * RB + ii;
+        if (r > k) {
+          const float l = Ls[r * LP + k];
+#pragma unroll
+          for (int kk = 0; kk < RB; ++kk) a[ii][kk] -= l * rv[kk];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int ii = 0; ii < RB; ++ii)
+#pragma unroll
+    for (int kk = 0; kk < RB; ++kk) Xs[(ty * RB + ii) * LP + tx * RB + kk] = a[ii][kk];
+  __syncthreads();
+
+  // ---- 3a. M = Y^T Y  (M[a][b] = sum_k Y[k][a] Y[k][b])
+  floatx16 acc[PER_WAVE];
+#pragma unroll
+  for (int x = 0; x < PER_WAVE; ++x) {
+    acc[x] = floatx16{};
+    const int blk = w * PER_WAVE + x;
+    if (blk < NBLK) {
+      const int ba = blk / NB, bb = blk % NB;
+      for (int s = 0; s < D / 2; ++s) {
+        const float av = Xs[(2 * s + hf) * LP + 32 * ba + j];
+        const float bv = Xs[(2 * s + hf) * LP + 32 * bb + j];
+        acc[x] = mfma_f32(av, bv, acc[x]);
+      }
+    }
+  }
+  __syncthreads();   // Ls (L) and Xs (Y) reads done
+#pragma unroll
+  for (int x = 0; x < PER_WAVE; ++x) {
+    const int blk = w * PER_WAVE + x;
+    if (blk < NBLK) {
+      const int ba = blk / NB, bb = blk % NB;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * ba + 8 * (r >> 2) + 4 * hf + (r & 3);
+        Ls[row * LP + 32 * bb + j] = acc[x][r];
+        Gp[row * D + 32 * bb + j] = acc[x][r];
+      }
+    }
+  }
+  for (int e = tid; e < D * D; e += 256) Xs[(e / D) * LP + (e % D)] = Bp[e];
+  __syncthreads();
+
+  // ---- 3b. C = beta B M  (C[a][b] = beta sum_k B[a][k] M[k][b])
+#pragma unroll
+  for (int x = 0; x < PER_WAVE; ++x) {
+    const int blk = w * PER_WAVE + x;
+    if (blk < NBLK) {
+      const int ba = blk / NB, bb = blk % NB;
+      floatx16 c = floatx16{};
+      for (int s = 0; s < D / 2; ++s) {
+        const float av = Xs[(32 * ba + j) * LP + 2 * s + hf];
+        const float bv = Ls[(2 * s + hf) * LP + 32 * bb + j];
+        c = mfma_f32(av, bv, c);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * ba + 8 * (r >> 2) + 4 * hf + (r & 3);
+        Bp[row * D + 32 * bb + j] = b * c[r];
+      }
+    }
+  }
+}
+
+// ============================================================ serial scan
+// grid (D/32 row blocks, 2 directions, H), D/32 waves.  Each workgroup carries
+// 32 rows of the state through every frame of its direction: the rows of
+// S <- S M + C evolve independently.  Wave w computes output columns
+// [32w, 32w+32) as S_new^T = M S^T + C^T with fp32 MFMA; the state is exchanged
+// between waves through LDS in the MFMA's own output layout.
+template <int D>
+__global__ __launch_bounds__(2 * D) void scan_kernel(const float* __restrict__ Mg,
+                                                     const float* __restrict__ Cg, int F, int H,
+                                                     float* __restrict__ Sf, float* __restrict__ Sb) {
+  constexpr int NW = D / 32;
+  constexpr int NT = 2 * D;                 // threads
+  constexpr int LP = D + 1;
+  constexpr int MCH = D * D / 4;            // float4 chunks of M
+  constexpr int MPER = MCH / NT;
+  __shared__ float Ms[D * LP];
+  __shared__ float Sx[NW * 16 * 64];
+
+  const int rb = blockIdx.x, dir = blockIdx.y, h = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, j = lane & 31, hf = lane >> 5;
+  const int C = num_chunks(F);
+  const int row = 32 * rb + j;
+  float* Sout = dir == 0 ? Sf : Sb;
+
+  auto snap = [&](int c, const floatx16& s) {
+    float* dst = Sout + (((size_t)c * H + h) * D + row) * D + 32 * w + 4 * hf;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4*>(dst + 8 * g) = make_float4(s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]);
+  };
+  // chunks whose set of frames is empty keep a zero state
+  const floatx16 zero = floatx16{};
+  for (int c = 0; c < C; ++c) {
+    const bool empty = dir == 0 ? (c <= 1) : (5 * c + 10 > F - 2);
+    if (empty) snap(c, zero);
+  }
+  int t0, nsteps, tstep;
+  if (dir == 0) {
+    t0 = 1;
+    nsteps = 5 * (C - 1) - 6;          // frames 1 .. 5(C-1)-6
+    tstep = 1;
+  } else {
+    t0 = F - 2;
+    nsteps = F - 2 - 10 + 1;           // frames F-2 down to 10
+    tstep = -1;
+  }
+  if (nsteps <= 0) return;
+
+  for (int x = tid; x < NW * 16 * 64; x += NT) Sx[x] = 0.f;
+  float4 mreg[MPER];
+  auto load_m = [&](int t) {
+    const float4* src = reinterpret_cast<const float4*>(Mg + ((size_t)t * H + h) * D * D);
+#pragma unroll
+    for (int x = 0; x < MPER; ++x) mreg[x] = src[tid + NT * x];
+  };
+  load_m(t0);
+  floatx16 acc = floatx16{};
+  for (int step = 0; step < nsteps; ++step) {
+    const int t = t0 + tstep * step;
+#pragma unroll
+    for (int x = 0; x < MPER; ++x) {
+      const int c4 = tid + NT * x;
+      const int r = (4 * c4) / D, col = (4 * c4) % D;
+      Ms[r * LP + col + 0] = mreg[x].x;
+      Ms[r * LP + col + 1] = mreg[x].y;
+      Ms[r * LP + col + 2] = mreg[x].z;
+      Ms[r * LP + col + 3] = mreg[x].w;
+    }
+    // C_t entries of this lane's outputs initialise the accumulator
+    {
+      const float* cp = Cg + (((size_t)t * H + h) * D + row) * D + 32 * w + 4 * hf;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 cv = *reinterpret_cast<const float4*>(cp + 8 * g);
+        acc[4 * g + 0] = cv.x;
+        acc[4 * g + 1] = cv.y;
+        acc[4 * g + 2] = cv.z;
+        acc[4 * g + 3] = cv.w;
+      }
+    }
+    __syncthreads();
+    if (step + 1 < nsteps) load_m(t + tstep);
+#pragma unroll 8
+    for (int s = 0; s < D / 2; ++s) {
+      const int wb = s >> 4, e = s & 15;
+      const int kap = 32 * wb + 8 * (e >> 2) + 4 * hf + (e & 3);
+      acc = mfma_f32(Ms[(32 * w + j) * LP + kap], Sx[(wb * 16 + e) * 64 + lane], acc);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Sx[(w * 16 + e) * 64 + lane] = acc[e];
+    if (dir == 0) {
+      if (t % 5 == 4) {
+        const int c = (t + 6) / 5;
+        if (c <= C - 1) snap(c, acc);
+      }
+    } else {
+      if (t % 5 == 0 && t >= 10) snap((t - 10) / 5, acc);
+    }
+  }
+}
+
+// ============================================================ readout weights
+// W[c][h] = diag(g_h) (S_fwd[c][h] + S_bwd[c][h]) (g = 1 when gate is null).
+// bf16 path: stored as bf16 hi and lo parts (hi = bf16(W), lo = bf16(W - hi)) so
+// the bf16 MFMA readout keeps ~16 mantissa bits of W; fp32 path: fp32.
+__global__ void wprep_kernel(const float* __restrict__ Sf, const float* __restrict__ Sb,
+                             const float* __restrict__ gate, int C, int H, int D, int bf16,
+                             void* __restrict__ W) {
+  const size_t n = (size_t)C * H * D * D;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const int dv = (i / D) % D;
+    const int h = (i / ((size_t)D * D)) % H;
+    const float g = gate ? gate[(size_t)h * D + dv] : 1.f;
+    const float x = g * (Sf[i] + Sb[i]);
+    if (bf16) {
+      const uint16_t hi = f32_to_bf16_bits(x);
+      const uint16_t lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+      uint16_t* Wb = static_cast<uint16_t*>(W);
+      Wb[i] = hi;
+      Wb[n + i] = lo;
+    } else {
+      static_cast<float*>(W)[i] = x;
+    }
+  }
+}
+
+// ============================================================ readout (bf16)
+// grid (RX, C, H), 256 threads.  Tokens of chunk c's non-anchor frames, tiles of
+// 128 (32 per wave).  O_lin^T = W q^T with W (hi and lo) resident in LDS and q as
+// the MFMA B operand; ACC: O += O_lin, else O = O_lin.
+template <int D, bool ACC>
+__global__ __launch_bounds__(256, 2) void readout_kernel(const uint16_t* __restrict__ q,
+                                                      const uint16_t* __restrict__ Wb, int F,
+                                                      int N, int H, uint16_t* __restrict__ O) {
+  constexpr int P = D + 8;
+  constexpr int NDB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][D * P];
+  const int c = blockIdx.y, h = blockIdx.z;
+  const int C = num_chunks(F);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, j = lane & 31, hf = lane >> 5;
+  const int tok_begin = nq_first(c) * N, tok_end = nq_end(c, F) * N;
+  if (tok_end <= tok_begin) return;
+  const size_t n = (size_t)C * H * D * D;
+  {
+    const uint16_t* src = Wb + ((size_t)c * H + h) * D * D;
+    for (int x = tid; x < 2 * D * D / 8; x += 256) {
+      const int part = x / (D * D / 8), cc = x % (D * D / 8);
+      const int r = (8 * cc) / D, col = (8 * cc) % D;
+      *reinterpret_cast<uint4*>(&Ws[part][r * P + col]) =
+          *reinterpret_cast<const uint4*>(src + part * n + 8 * cc);
+    }
+  }
+  __syncthreads();
+  const size_t rs = (size_t)H * D;
+  const int ntile = (tok_end - tok_begin + 127) / 128;
+  for (int tile = blockIdx.x; tile < ntile; tile += gridDim.x) {
+    // keep W's fragments in LDS: re-read them per tile instead of pinning
+    // D*D/32 registers per lane for the whole loop
+    asm volatile("" ::: "memory");
+    const int tok = tok_begin + tile * 128 + 32 * w + j;
+    const bool valid = tok < tok_end;
+    const size_t off = (size_t)tok * rs + (size_t)h * D;
+    bf16x8 qb[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qb[s] = valid ? *reinterpret_cast<const bf16x8*>(q + off + 16 * s + 8 * hf) : bf16x8{};
+#pragma unroll
+    for (int ab = 0; ab < NDB; ++ab) {
+      floatx16 acc = floatx16{};
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const bf16x8 whi = *reinterpret_cast<const bf16x8*>(&Ws[0][(32 * ab + j) * P + 16 * s + 8 * hf]);
+        const bf16x8 wlo = *reinterpret_cast<const bf16x8*>(&Ws[1][(32 * ab + j) * P + 16 * s + 8 * hf]);
+        acc = mfma_bf16(whi, qb[s], acc);
+        acc = mfma_bf16(wlo, qb[s], acc);
+      }
+      if (valid) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          uint16_t* dst = O + off + 32 * ab + 8 * g + 4 * hf;
+          float x0 = acc[4 * g], x1 = acc[4 * g + 1], x2 = acc[4 * g + 2], x3 = acc[4 * g + 3];
+          if (ACC) {
+            const uint2 old = *reinterpret_cast<const uint2*>(dst);
+            x0 += __uint_as_float(old.x << 16);
+            x1 += __uint_as_float(old.x & 0xffff0000u);
+            x2 += __uint_as_float(old.y << 16);
+            x3 += __uint_as_float(old.y & 0xffff0000u);
+          }
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
+        }
+      }
+    }
+  }
+}
+
+// ============================================================ readout (fp32)
+// One thread per output element of a non-anchor frame.
+template <bool ACC>
+__global__ void readout_f32_kernel(const float* __restrict__ q, const float* __restrict__ W, int F,
+                                   int N, int H, int D, float* __restrict__ O) {
+  const size_t total = (size_t)F * N * H * D;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int dv = i % D;
+    const int h = (i / D) % H;
+    const size_t tok = i / ((size_t)H * D);
+    const int f = static_cast<int>(tok / N);
+    if (f == 0 || f == F - 1) continue;
+    const int c = f / kChunk;
+    const float* wr = W + (((size_t)c * H + h) * D + dv) * D;
+    const float* qr = q + tok * H * D + (size_t)h * D;
+    float s = 0.f;
+    for (int kk = 0; kk < D; ++kk) s += wr[kk] * qr[kk];
+    O[i] = ACC ? O[i] + s : s;
+  }
+}
+
+__global__ void fill_zero_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// ============================================================ launchers
+hipError_t launch_gram_f32(const float* k, const float* v, int F, int N, int H, int D, float* G,
+                           float* B, hipStream_t st) {
+  const dim3 grid(F, H);
+  switch (D) {
+    case 32: hipLaunchKernelGGL(gram_f32_kernel<32>, grid, dim3(256), 0, st, k, v, F, N, H, G, B); break;
+    case 64: hipLaunchKernelGGL(gram_f32_kernel<64>, grid, dim3(256), 0, st, k, v, F, N, H, G, B); break;
+    case 128: hipLaunchKernelGGL(gram_f32_kernel<128>, grid, dim3(256), 0, st, k, v, F, N, H, G, B); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t factor_d(float* G, float* B, const float* beta, int F, int H, hipStream_t st) {
+  const size_t lds = (2 * (size_t)D * (D + 1) + 2 * D) * sizeof(float);
+  static bool attr_done = false;
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&factor_kernel<D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  hipLaunchKernelGGL(factor_kernel<D>, dim3(F - 2, H), dim3(256), lds, st, G, B, beta, F, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_factor(float* G, float* B, const float* beta, int F, int H, int D, hipStream_t st) {
+  if (F < 3) return hipSuccess;
+  switch (D) {
+    case 32: return factor_d<32>(G, B, beta, F, H, st);
+    case 64: return factor_d<64>(G, B, beta, F, H, st);
+    case 128: return factor_d<128>(G, B, beta, F, H, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_scan(const float* M, const float* Cm, int F, int H, int D, float* Sf, float* Sb,
+                       hipStream_t st) {
+  const dim3 grid(D / 32, 2, H);
+  switch (D) {
+    case 32: hipLaunchKernelGGL(scan_kernel<32>, grid, dim3(64), 0, st, M, Cm, F, H, Sf, Sb); break;
+    case 64: hipLaunchKernelGGL(scan_kernel<64>, grid, dim3(128), 0, st, M, Cm, F, H, Sf, Sb); break;
+    case 128: hipLaunchKernelGGL(scan_kernel<128>, grid, dim3(256), 0, st, M, Cm, F, H, Sf, Sb); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_wprep(const float* Sf, const float* Sb, const float* gate, int C, int H, int D,
+                        int bf16, void* W, hipStream_t st) {
+  const size_t n = (size_t)C * H * D * D;
+  const unsigned blocks = (unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
+  hipLaunchKernelGGL(wprep_kernel, dim3(blocks), dim3(256), 0, st, Sf, Sb, gate, C, H, D, bf16, W);
+  return hipGetLastError();
+}
+
+hipError_t launch_readout(int prec, const void* q, const void* W, int F, int N, int H, int D,
+                          void* O, int accumulate, hipStream_t st) {
+  const int C = num_chunks(F);
+  if (prec == 0) {
+    const size_t total = (size_t)F * N * H * D;
+    const unsigned blocks = (unsigned)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+    if (accumulate)
+      hipLaunchKernelGGL(readout_f32_kernel<true>, dim3(blocks), dim3(256), 0, st,
+                         static_cast<const float*>(q), static_cast<const float*>(W), F, N, H, D, static_cast<float*>(O));
+    else
+      hipLaunchKernelGGL(readout_f32_kernel<false>, dim3(blocks), dim3(256), 0, st,
+                         static_cast<const float*>(q), static_cast<const float*>(W), F, N, H, D, static_cast<float*>(O));
+    return hipGetLastError();
+  }
+  const int max_tiles = (kChunk * N + 127) / 128;
+  const int rx = max_tiles < 8 ? max_tiles : 8;
+  const dim3 grid(rx, C, H);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* ww = static_cast<const uint16_t*>(W);
+  uint16_t* oo = static_cast<uint16_t*>(O);
+#define VDN_RO(DD)                                                                                        \
+  if (D == DD) {                                                                                          \
+    if (accumulate)                                                                                       \
+      hipLaunchKernelGGL((readout_kernel<DD, true>), grid, dim3(256), 0, st, qq, ww, F, N, H, oo);        \
+    else                                                                                                  \
+      hipLaunchKernelGGL((readout_kernel<DD, false>), grid, dim3(256), 0, st, qq, ww, F, N, H, oo);       \
+    return hipGetLastError();                                                                             \
+  }
+  VDN_RO(32) VDN_RO(64) VDN_RO(128)
+#undef VDN_RO
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t st) {
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, st, static_cast<uint32_t*>(p), n);
+  return hipGetLastError();
+}
+
+}  // namespace vdn

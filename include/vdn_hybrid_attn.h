@@ -1,0 +1,156 @@
+/*
+ * vdn_hybrid_attn.h -- C ABI of the Video DeltaNet (VDN) hybrid video-to-video
+ * attention layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (arXiv abstract page "Video DeltaNet: A Video-Native Hybrid Attention
+ * for Livestream Video Generation", Abstract; sd114.wiki article "VDN-Minimax-H3 ...",
+ * sections 双向滑动窗口Softmax分支 and 双向线性注意力分支) combines
+ *   (a) softmax attention over a block-sliding window: five latent frames form a
+ *       chunk, a chunk attends to itself and to its previous and next chunk, every
+ *       frame also attends to all tokens of the first and last frame, and the first
+ *       and last frame attend to every frame;
+ *   (b) a bidirectional linear branch, Video Delta Attention (VDA), whose memory is
+ *       updated once per frame by all of the frame's tokens jointly; for query frame
+ *       i the forward state summarises the frames before its window and the backward
+ *       state the frames after it (never the window or the anchor frames), and the
+ *       query reads both and adds the results;
+ *   (c) a gated merge of the two branches (besthub article "VDN-H3 Generates
+ *       14-Second 768p Video ...", section Hybrid Attention Architecture).
+ * The pages give no algebra for the VDA update; this library implements the
+ * proximal least-squares step
+ *       S_t = (S_{t-1} + beta_t V_t K_t^T) (I + beta_t K_t K_t^T)^-1,
+ * with K_t, V_t the d x N keys and values of frame t as columns, S_0 = 0, and the
+ * readout o = S_fwd q + S_bwd q.  The merge is O = O_soft + g (.) O_lin with a
+ * per-(head, channel) gate g.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors q, k, v, O are [F, N, H, d] row-major: F latent frames, N tokens per
+ *     frame, H heads, head dim d; one token's H*d values are contiguous.
+ *     Element type by `precision`: fp32 for VDN_PREC_FP32, bf16 (raw 16-bit
+ *     bfloat16 bit patterns) for VDN_PREC_BF16 and VDN_PREC_BF16_FP8QK.
+ *   - beta is fp32 [F, H], gate is fp32 [H, d], states are fp32 [C, H, d, d] with
+ *     C = ceil(F / 5) chunks; state row = value channel, column = key channel.
+ *   - Every pointer except the host-side `table` of vdn_schedule is a DEVICE
+ *     pointer (HIP global memory on the current device), owned by the caller; the
+ *     library neither allocates nor frees memory and keeps no state across calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *     work: the return status covers argument checks and kernel launches; results
+ *     are valid once the stream has been synchronised, and inputs must stay
+ *     unchanged until then.  Outputs must not alias inputs.
+ *   - `workspace` is caller-owned device scratch of at least
+ *     vdn_workspace_bytes(F, N, H, d, precision) bytes, 256-byte aligned; it holds
+ *     no meaning between calls.  Calls that share a workspace must not overlap.
+ *   - Supported: F >= 1, N >= 1, H >= 1, d in {32, 64, 128}; VDN_PREC_BF16_FP8QK
+ *     needs d in {64, 128}.  Anything else returns an error and launches nothing.
+ *   - Results are deterministic: no atomics take part in value reductions.
+ */
+#ifndef VDN_HYBRID_ATTN_H
+#define VDN_HYBRID_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define VDN_OK                0
+#define VDN_ERR_INVALID_ARG  (-1)  /* null pointer, non-positive size, misaligned buffer */
+#define VDN_ERR_UNSUPPORTED  (-2)  /* valid but unsupported (d, precision) combination   */
+#define VDN_ERR_WORKSPACE    (-3)  /* workspace smaller than vdn_workspace_bytes()      */
+#define VDN_ERR_HIP          (-4)  /* a HIP call failed; see vdn_last_hip_error()       */
+
+/* Precisions. */
+#define VDN_PREC_FP32        0     /* q, k, v, O fp32; fp32 arithmetic                      */
+#define VDN_PREC_BF16        1     /* q, k, v, O bf16; fp32 accumulation                    */
+#define VDN_PREC_BF16_FP8QK  2     /* bf16 I/O; the softmax branch's q.k products use OCP
+                                      E4M3 codes with per-head scales amax/448 computed
+                                      internally; P.V, the VDA branch and the merge as bf16 */
+
+/* Bytes of workspace the calls below need for this shape; 0 if the shape or
+ * precision is invalid or unsupported. */
+size_t vdn_workspace_bytes(int F, int N, int H, int d, int precision);
+
+/* The whole hybrid layer: O = O_soft + g (.) O_lin.
+ * Cited definition: see the header comment (all three parts).
+ * q, k, v, O: [F, N, H, d]; beta: [F, H] (beta_t > 0 for a meaningful update);
+ * gate: [H, d].  O must not alias q, k or v. */
+int vdn_hybrid_attn(const void* q, const void* k, const void* v,
+                    const float* beta, const float* gate,
+                    int F, int N, int H, int d, int precision,
+                    void* O, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Softmax branch alone (part (a)): O_soft[i, n, h] = sum over tokens (j, m) of
+ * the key frames of query frame i of softmax_{(j,m)}(q_{i,n,h} . k_{j,m,h} / sqrt(d))
+ * v_{j,m,h}, with the window + anchor frame sets of the sd114.wiki article,
+ * section 双向滑动窗口Softmax分支.  Same layouts as vdn_hybrid_attn. */
+int vdn_softmax_branch(const void* q, const void* k, const void* v,
+                       int F, int N, int H, int d, int precision,
+                       void* O_soft, void* workspace, size_t workspace_bytes, void* stream);
+
+/* VDA states alone (part (b), memory side): S_fwd[c, h] is the state after the
+ * frames before chunk c's window (ascending, anchors excluded), S_bwd[c, h] the
+ * state after the frames after the window (absorbed latest first); zero where
+ * the set is empty (sd114.wiki article, section 双向线性注意力分支; besthub
+ * article, section Video Delta Attention (VDA)).
+ * k, v: [F, N, H, d]; beta: [F, H]; S_fwd, S_bwd: fp32 [C, H, d, d] outputs. */
+int vdn_vda_states(const void* k, const void* v, const float* beta,
+                   int F, int N, int H, int d, int precision,
+                   float* S_fwd, float* S_bwd,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* VDA readout alone (part (b), query side): O_lin[i, n, h] = (S_fwd[c(i), h] +
+ * S_bwd[c(i), h]) q[i, n, h] for non-anchor frames i (c(i) = i / 5), and 0 on the
+ * first and last frame.  Ungated.  q, O_lin: [F, N, H, d] in the precision's I/O
+ * type; S_fwd, S_bwd: fp32 [C, H, d, d].  Needs no workspace beyond
+ * vdn_workspace_bytes (the same workspace convention applies). */
+int vdn_vda_linear(const void* q, const float* S_fwd, const float* S_bwd,
+                   int F, int N, int H, int d, int precision,
+                   void* O_lin, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The fp8 quantiser of VDN_PREC_BF16_FP8QK, exposed for byte-exact checks:
+ * amax[h] = max |x| over head h (fp32), code = E4M3(RNE, saturating) of
+ * fp32(x * fp32(448 / amax[h])) (0 where amax is 0).  x: bf16 [F, N, H, d];
+ * codes: uint8 [F, N, H, d] (OCP E4M3 "FN" bit patterns); amax: fp32 [H]. */
+int vdn_fp8_quantize(const void* x, int F, int N, int H, int d,
+                     unsigned char* codes, float* amax, void* stream);
+
+/* Frame partition of the layer for F frames (host only, no device work).
+ * One row of VDN_SCHED_COLS ints per group of query frames that share their
+ * sets: { q_first, q_last, n_soft,  s0_first, s0_last, s1_first, s1_last,
+ *         s2_first, s2_last,  fwd_first, fwd_last, bwd_first, bwd_last }
+ * (frame indices, inclusive; unused softmax ranges and empty linear sets are
+ * -1, -1).  Rows: the first frame, each chunk's non-anchor frames, the last
+ * frame, in ascending q_first.  Writes at most `cap` rows to `table` (may be
+ * NULL when cap is 0) and returns the number of rows, or a negative status. */
+#define VDN_SCHED_COLS 13
+int vdn_schedule(int F, int* table, int cap);
+
+/* Stages of the launch sequence, for vdn_set_stage_events. */
+#define VDN_STAGE_PREP     0   /* one pass over k, v: v re-laid out for P.V, frame Grams */
+#define VDN_STAGE_FACTOR   1   /* per-frame Cholesky: M_t = A_t^-1, C_t = beta B_t M_t     */
+#define VDN_STAGE_SCAN     2   /* serial state scan, both directions                     */
+#define VDN_STAGE_WPREP    3   /* readout weights g (.) (S_fwd + S_bwd)                   */
+#define VDN_STAGE_ATTN     4   /* windowed + anchored softmax attention                  */
+#define VDN_STAGE_COMBINE  5   /* merge of the anchor rows' key slices                   */
+#define VDN_STAGE_READOUT  6   /* linear readout + gated merge                           */
+#define VDN_STAGE_QUANT    7   /* fp8 quantiser of q and k                               */
+#define VDN_NUM_STAGES     8
+
+/* Measurement aid for the calling thread: while set, every entry point records
+ * the hipEvent_t `before` on its stream immediately before it enqueues the
+ * kernels of `stage`, and `after` immediately after.  The events are created
+ * and owned by the caller; pass NULL, NULL to stop recording.  Returns VDN_OK or
+ * VDN_ERR_INVALID_ARG for an unknown stage. */
+int vdn_set_stage_events(int stage, void* before, void* after);
+
+/* Human-readable text of a status code (static storage). */
+const char* vdn_status_string(int status);
+
+/* The hipError_t of the last failed HIP call on the calling thread (0 if none). */
+int vdn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VDN_HYBRID_ATTN_H */

@@ -119,11 +119,12 @@ def _softmax_rows(s: np.ndarray) -> np.ndarray:
     return p / p.sum(axis=-1, keepdims=True)
 
 
-def softmax_branch(q, k, v, frames=None, heads=None) -> np.ndarray:
+def softmax_branch(q, k, v, frames=None, heads=None, tokens=None) -> np.ndarray:
     """Windowed + anchored softmax attention, one query frame at a time.
 
-    Returns float64 [len(frames), N, len(heads), d] for the requested query
-    frames and heads (all by default).  q, k, v: [F, N, H, d].
+    Returns float64 [len(frames), len(tokens), len(heads), d] for the requested
+    query frames, query tokens within a frame and heads (all by default).
+    q, k, v: [F, N, H, d].
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -131,12 +132,13 @@ def softmax_branch(q, k, v, frames=None, heads=None) -> np.ndarray:
     F, N, H, d = q.shape
     frames = list(range(F)) if frames is None else list(frames)
     heads = list(range(H)) if heads is None else list(heads)
-    out = np.zeros((len(frames), N, len(heads), d))
+    tokens = list(range(N)) if tokens is None else list(tokens)
+    out = np.zeros((len(frames), len(tokens), len(heads), d))
     for a, h in enumerate(heads):
         for b, i in enumerate(frames):
             keys = np.concatenate([k[j, :, h, :] for j in softmax_frames(i, F)], axis=0)
             vals = np.concatenate([v[j, :, h, :] for j in softmax_frames(i, F)], axis=0)
-            p = _softmax_rows(q[i, :, h, :] @ keys.T / math.sqrt(d))
+            p = _softmax_rows(q[i, tokens, h, :] @ keys.T / math.sqrt(d))
             out[b, :, a, :] = p @ vals
     return out
 
