@@ -162,35 +162,33 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
 
-    nst = len(vdn.STAGES)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(nst)] for _ in range(args.steps)]
+    # stages the layer runs in this precision
+    run = [st for st, name in enumerate(vdn.STAGES) if name != "quant" or prec == "bf16_fp8qk"]
+    ev = {(s, st): (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for s in range(args.steps) for st in run}
+    for pair in ev.values():       # torch creates the HIP event on its first record
+        pair[0].record()
+        pair[1].record()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
     for s in range(args.steps):
-        for st in range(nst):
-            vdn.set_stage_events(st, ev[s][st][0], ev[s][st][1])
+        for st in run:
+            vdn.set_stage_events(st, *ev[(s, st)])
         step()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    for st in range(nst):
+    for st in run:
         vdn.set_stage_events(st, None, None)
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
     stages = {}
-    for st, name in enumerate(vdn.STAGES):
-        vals = []
-        for s in range(args.steps):
-            try:
-                vals.append(ev[s][st][0].elapsed_time(ev[s][st][1]))
-            except RuntimeError:        # stage not run in this precision
-                pass
-        if vals:
-            stages[name] = sum(vals) / len(vals)
+    for st in run:
+        vals = [ev[(s, st)][0].elapsed_time(ev[(s, st)][1]) for s in range(args.steps)]
+        stages[vdn.STAGES[st]] = sum(vals) / len(vals)
     print(f"[bench] {args.steps} steps: {ms:.2f} ms/step (wall {1000 * wall / args.steps:.2f})",
           file=sys.stderr, flush=True)
 

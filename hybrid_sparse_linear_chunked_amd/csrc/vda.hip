@@ -269,11 +269,14 @@ __global__ __launch_bounds__(2 * D) void scan_kernel(const float* __restrict__ M
     for (int g = 0; g < 4; ++g)
       *reinterpret_cast<float4*>(dst + 8 * g) = make_float4(s[4 * g], s[4 * g + 1], s[4 * g + 2], s[4 * g + 3]);
   };
-  // chunks whose set of frames is empty keep a zero state
+  // A chunk's state is zero when its set of frames is empty, and also when the
+  // chunk holds no non-anchor frame (the last chunk when F = 5m + 1): no query
+  // reads such a state.
+  auto live = [&](int c) { return nq_end(c, F) > nq_first(c); };
   const floatx16 zero = floatx16{};
   for (int c = 0; c < C; ++c) {
     const bool empty = dir == 0 ? (c <= 1) : (5 * c + 10 > F - 2);
-    if (empty) snap(c, zero);
+    if (empty || !live(c)) snap(c, zero);
   }
   int t0, nsteps, tstep;
   if (dir == 0) {
@@ -333,10 +336,10 @@ __global__ __launch_bounds__(2 * D) void scan_kernel(const float* __restrict__ M
     if (dir == 0) {
       if (t % 5 == 4) {
         const int c = (t + 6) / 5;
-        if (c <= C - 1) snap(c, acc);
+        if (c <= C - 1 && live(c)) snap(c, acc);
       }
     } else {
-      if (t % 5 == 0 && t >= 10) snap((t - 10) / 5, acc);
+      if (t % 5 == 0 && t >= 10 && live((t - 10) / 5)) snap((t - 10) / 5, acc);
     }
   }
 }

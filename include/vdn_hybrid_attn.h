@@ -91,8 +91,9 @@ int vdn_softmax_branch(const void* q, const void* k, const void* v,
 /* VDA states alone (part (b), memory side): S_fwd[c, h] is the state after the
  * frames before chunk c's window (ascending, anchors excluded), S_bwd[c, h] the
  * state after the frames after the window (absorbed latest first); zero where
- * the set is empty (sd114.wiki article, section 双向线性注意力分支; besthub
- * article, section Video Delta Attention (VDA)).
+ * the set is empty, and zero for a chunk that holds no non-anchor frame (the
+ * last chunk when F = 5m + 1), whose state no query reads (sd114.wiki article,
+ * section 双向线性注意力分支; besthub article, section Video Delta Attention (VDA)).
  * k, v: [F, N, H, d]; beta: [F, H]; S_fwd, S_bwd: fp32 [C, H, d, d] outputs. */
 int vdn_vda_states(const void* k, const void* v, const float* beta,
                    int F, int N, int H, int d, int precision,
