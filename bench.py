@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=3, choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 3 device-to-device copies of MIB MiB (a known-size kernel "
+                         "that calibrates the HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -132,6 +135,16 @@ def main():
     import torch
     import hybrid_sparse_linear_chunked_amd as vdn
     import vdn_synth
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return
 
     cfg = CONFIGS[args.config]
     F, N, H, d, prec = cfg["F"], cfg["N"], cfg["H"], cfg["d"], cfg["precision"]

@@ -158,6 +158,7 @@ struct AttnArgs {
 
 constexpr int BQ = 128;   // queries per work item (4 waves x 32)
 constexpr int BK = 64;    // keys per tile
+constexpr float kLazy = 8.f;   // log2 headroom before the running max is raised
 
 template <int D, int PREC>
 struct AttnCfg {
@@ -206,14 +207,26 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   int h, q_tok0, q_rows, split = -1, anchor_idx = 0;
   int kf_mode;          // 0: contiguous frames [k_f0, k_f1); 1: chunk key list
   int k_f0 = 0, k_f1 = 0, wf = 0, we = 0, nslots;
-  int bid = blockIdx.x;
+  // The dispatcher deals workgroups round-robin over the 8 XCDs (each with its own
+  // L2).  Renumber so that every XCD runs one contiguous range of work items:
+  // consecutive items share their key frames, so concurrent workgroups on an XCD
+  // stream the same K / V^T tiles through that XCD's L2.
+  int bid;
+  {
+    const int G = gridDim.x, b = blockIdx.x;
+    const int x = b & 7, i8 = b >> 3, q8 = G >> 3, r8 = G & 7;
+    bid = (x < r8 ? x * (q8 + 1) : r8 * (q8 + 1) + (x - r8) * q8) + i8;
+  }
   if (bid < a.n_anchor_items) {
-    split = bid % a.nsplit;
-    int r = bid / a.nsplit;
+    // anchor items: query tile fastest, then anchor frame, then key slice, then
+    // head, so items reading the same key slice are adjacent
+    int r = bid;
     const int qt = r % a.qt_anchor;
     r /= a.qt_anchor;
     anchor_idx = r % a.na;
-    h = r / a.na;
+    r /= a.na;
+    split = r % a.nsplit;
+    h = r / a.nsplit;
     const int qf = anchor_idx == 0 ? 0 : F - 1;
     q_tok0 = qf * N + qt * BQ;
     q_rows = min(BQ, N - qt * BQ);
@@ -412,34 +425,46 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
         }
       }
     }
-    // mask keys past the frame's end; scale to log2 units
+    // Online softmax in log2 units.  Scores are scaled inside the exp2 argument
+    // (one FMA).  The running max m_run is raised only when a tile's max exceeds it
+    // by more than kLazy (wave-uniform decision), so O and l are rescaled rarely;
+    // in between, p = 2^(x - m_run) <= 2^kLazy, which bf16 P and fp32 sums hold
+    // exactly as well as values <= 1.  The result O / l does not depend on m_run.
+    if (nvalid < BK) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key >= nvalid) s[kb][r] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-        float x = s[kb][r] * scale;
-        if (nvalid < BK && key >= nvalid) x = -INFINITY;
-        s[kb][r] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    const float mt = mx * scale;
+    if (__any(mt > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int x = 0; x < NDB; ++x) o[x] *= alpha;
+    }
+    const float neg_m = -m_run;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][r] - m_new);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale, neg_m));
         s[kb][r] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int x = 0; x < NDB; ++x) o[x] *= alpha;
+    l_run += psum;
 
     // O^T += V^T P^T
     if constexpr (F32) {
