@@ -19,6 +19,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # hipcc -O3 forms packed fp32 instructions on its own; keep them off
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no NaNs flow through the kernels: lets max/min skip NaN-quieting copies
+    "-fno-honor-nans", "-mno-amdgpu-ieee",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wno-unused-command-line-argument",
 ]

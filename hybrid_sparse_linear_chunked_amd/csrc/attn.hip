@@ -536,6 +536,305 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   }
 }
 
+// ============================================================ attention, bf16 / fp8
+// Same work items and arithmetic as attn_kernel, with K and V^T tiles moved
+// global -> LDS by the 16-byte direct loads of gfx950 (global_load_lds_dwordx4):
+// no staging registers, no LDS store instructions.  A direct load writes the 64
+// lanes' 16-byte pieces to 1 KiB of consecutive LDS, so bank conflicts are
+// avoided with an XOR swizzle of the 16-byte chunks inside a row instead of row
+// padding: chunk c of row r sits at position c ^ swz(r).
+template <int D, int PREC>
+struct LdsCfg {
+  static constexpr bool FP8 = PREC == 2;
+  static constexpr int KROW = FP8 ? D : 2 * D;     // bytes per K row
+  static constexpr int KCH = KROW / 16;            // 16-byte chunks per K row
+  static constexpr int K_BYTES = BK * KROW;
+  static constexpr int V_BYTES = D * BK * 2;       // V^T: D rows x 64 keys bf16 (128 B)
+  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int K_INSTR = K_BYTES / 1024;   // wave-wide direct loads per K tile
+  static constexpr int V_INSTR = V_BYTES / 1024;
+  static constexpr int K_RPI = 1024 / KROW;        // K rows per direct load
+  static constexpr int QSTEPS = FP8 ? D / 64 : D / 16;
+  static_assert(K_INSTR % 4 == 0 && V_INSTR % 4 == 0, "tiles split over 4 waves");
+  // 8 consecutive rows must land on distinct 16-byte bank groups
+  __device__ static int swz_k(int r) { return KROW >= 128 ? (r & 7) : ((r >> 1) & 3); }
+  __device__ static int swz_v(int r) { return r & 7; }
+};
+
+struct Item {
+  int h, q_tok0, q_rows, split, anchor_idx;
+  int mode;          // 0: frames [k_f0, k_f0 + nslots); 1: chunk key list
+  int k_f0, wf, we, nslots;
+};
+
+// Work item of this workgroup (same numbering as attn_kernel).
+__device__ inline Item decode_item(const AttnArgs& a) {
+  Item it;
+  const int F = a.F, N = a.N;
+  int bid;
+  {
+    const int G = gridDim.x, b = blockIdx.x;
+    const int x = b & 7, i8 = b >> 3, q8 = G >> 3, r8 = G & 7;
+    bid = (x < r8 ? x * (q8 + 1) : r8 * (q8 + 1) + (x - r8) * q8) + i8;
+  }
+  it.wf = it.we = it.k_f0 = 0;
+  if (bid < a.n_anchor_items) {
+    int r = bid;
+    const int qt = r % a.qt_anchor;
+    r /= a.qt_anchor;
+    it.anchor_idx = r % a.na;
+    r /= a.na;
+    it.split = r % a.nsplit;
+    it.h = r / a.nsplit;
+    const int qf = it.anchor_idx == 0 ? 0 : F - 1;
+    it.q_tok0 = qf * N + qt * BQ;
+    it.q_rows = min(BQ, N - qt * BQ);
+    it.mode = 0;
+    it.k_f0 = it.split * a.fs;
+    it.nslots = min(F, it.k_f0 + a.fs) - it.k_f0;
+  } else {
+    int r = bid - a.n_anchor_items;
+    it.split = -1;
+    it.anchor_idx = 0;
+    it.h = r / a.tiles_per_head;
+    r -= it.h * a.tiles_per_head;
+    const int C = num_chunks(F);
+    int c = 0;
+    for (; c < C; ++c) {
+      const int nf = nq_end(c, F) - nq_first(c);
+      const int t = nf > 0 ? (nf * N + BQ - 1) / BQ : 0;
+      if (r < t) break;
+      r -= t;
+    }
+    const int tok_begin = nq_first(c) * N, tok_end = nq_end(c, F) * N;
+    it.q_tok0 = tok_begin + r * BQ;
+    it.q_rows = min(BQ, tok_end - it.q_tok0);
+    it.mode = 1;
+    it.wf = win_first(c);
+    it.we = win_end(c, F);
+    it.nslots = (it.wf > 0 ? 1 : 0) + (it.we - it.wf) + (it.we < F ? 1 : 0);
+  }
+  return it;
+}
+
+template <int D, int PREC>
+__global__ __launch_bounds__(256, 2) void attn_lds_kernel(AttnArgs a) {
+  using Cfg = LdsCfg<D, PREC>;
+  constexpr bool FP8 = Cfg::FP8;
+  constexpr int NDB = D / 32;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int j = lane & 31, hf = lane >> 5;
+  const int F = a.F, N = a.N, H = a.H;
+  const size_t rs = (size_t)H * D;                 // token stride in elements
+  const int nb = (N + BK - 1) / BK;
+  const Item it = decode_item(a);
+  const int h = it.h;
+  const int ntiles = it.nslots * nb;
+
+  // ---- Q operand fragments, resident for the whole item
+  const int qi = 32 * w + j;
+  const bool qvalid = qi < it.q_rows;
+  const size_t qoff = (size_t)(it.q_tok0 + qi) * rs + (size_t)h * D;
+  bf16x8 qb[FP8 ? 1 : Cfg::QSTEPS];
+  intx8 q8f[FP8 ? Cfg::QSTEPS : 1];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int s = 0; s < Cfg::QSTEPS; ++s) {
+      if (qvalid) {
+        const uint4* p = reinterpret_cast<const uint4*>(a.q8 + qoff + 64 * s + 32 * hf);
+        const uint4 x0 = p[0], x1 = p[1];
+        q8f[s] = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      } else {
+        q8f[s] = intx8{};
+      }
+    }
+  } else {
+    const uint16_t* q = static_cast<const uint16_t*>(a.q);
+#pragma unroll
+    for (int s = 0; s < Cfg::QSTEPS; ++s)
+      qb[s] = qvalid ? *reinterpret_cast<const bf16x8*>(q + qoff + 16 * s + 8 * hf) : bf16x8{};
+  }
+  float scale = a.scale_log2;
+  if constexpr (FP8) scale *= (a.amax[h] * (1.f / 448.f)) * (a.amax[H + h] * (1.f / 448.f));
+
+  // ---- direct global -> LDS tile loads
+  const unsigned char* kbase = FP8 ? reinterpret_cast<const unsigned char*>(a.k8)
+                                   : static_cast<const unsigned char*>(a.k);
+  auto frame_of = [&](int slot) {
+    return it.mode == 0 ? it.k_f0 + slot : chunk_key_frame(slot, it.wf, it.we, F);
+  };
+  auto issue_tile = [&](int stage, int f, int b) {
+    unsigned char* sbase = smem + stage * Cfg::STAGE;
+    const int nvalid = min(BK, N - BK * b);
+    const size_t tok0 = (size_t)f * N + BK * b;
+#pragma unroll
+    for (int x = 0; x < Cfg::K_INSTR / 4; ++x) {
+      const int ii = w * (Cfg::K_INSTR / 4) + x;
+      const int r = ii * Cfg::K_RPI + lane / Cfg::KCH;
+      const int c = (lane % Cfg::KCH) ^ Cfg::swz_k(r);
+      const int n = min(r, nvalid - 1);               // rows past the frame: any valid row
+      const unsigned char* src = kbase + ((tok0 + n) * rs + (size_t)h * D) * (FP8 ? 1 : 2) + 16 * c;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(sbase + 1024 * ii), 16, 0, 0);
+    }
+    const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(
+        a.vt + (((size_t)h * F + f) * nb + b) * (size_t)(D * BK));
+#pragma unroll
+    for (int x = 0; x < Cfg::V_INSTR / 4; ++x) {
+      const int ii = w * (Cfg::V_INSTR / 4) + x;
+      const int r = ii * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ Cfg::swz_v(r);
+      __builtin_amdgcn_global_load_lds(vsrc + r * 128 + 16 * c,
+                                       (lds_void_ptr)(sbase + Cfg::K_BYTES + 1024 * ii), 16, 0, 0);
+    }
+  };
+
+  floatx16 o[NDB];
+#pragma unroll
+  for (int x = 0; x < NDB; ++x) o[x] = floatx16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  int slot = 0, b = 0, f = frame_of(0);
+  issue_tile(0, f, b);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int stage = t & 1;
+    int nslot = slot, nbk = b + 1;
+    if (nbk == nb) {
+      nbk = 0;
+      ++nslot;
+    }
+    int nf = f;
+    if (t + 1 < ntiles) {
+      nf = nbk == 0 ? frame_of(nslot) : f;
+      issue_tile(stage ^ 1, nf, nbk);
+    }
+    const int nvalid = min(BK, N - BK * b);
+    const unsigned char* sbase = smem + stage * Cfg::STAGE;
+
+    // ---- S^T = K Q^T for two 32-key blocks
+    floatx16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = floatx16{};
+      const int r = 32 * kb + j;
+      const unsigned char* krow = sbase + r * Cfg::KROW;
+      const int sw = Cfg::swz_k(r);
+      if constexpr (FP8) {
+#pragma unroll
+        for (int st = 0; st < Cfg::QSTEPS; ++st) {
+          const int c0 = 4 * st + 2 * hf;
+          const uint4 x0 = *reinterpret_cast<const uint4*>(krow + 16 * (c0 ^ sw));
+          const uint4 x1 = *reinterpret_cast<const uint4*>(krow + 16 * ((c0 + 1) ^ sw));
+          const intx8 ka = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+          s[kb] = mfma_fp8(ka, q8f[st], s[kb]);
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < Cfg::QSTEPS; ++st) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 16 * ((2 * st + hf) ^ sw));
+          s[kb] = mfma_bf16(ka, qb[st], s[kb]);
+        }
+      }
+    }
+
+    // ---- online softmax (see attn_kernel)
+    if (nvalid < BK) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key >= nvalid) s[kb][r] = -INFINITY;
+        }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int e = 1; e < 31; e += 2)
+      mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[e >> 4][e & 15]), s[(e + 1) >> 4][(e + 1) & 15]);
+    mx = __builtin_fmaxf(mx, s[1][15]);
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    const float mt = mx * scale;
+    if (__any(mt > m_run + kLazy)) {
+      const float m_new = __builtin_fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int x = 0; x < NDB; ++x) o[x] *= alpha;
+    }
+    const float neg_m = -m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale, neg_m));
+        s[kb][r] = p;
+        psum += p;
+      }
+    l_run += psum;
+
+    // ---- O^T += V^T P^T
+    const unsigned char* vbase = sbase + Cfg::K_BYTES;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kb = u >> 1, e0 = 8 * (u & 1);
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[kb][e0 + e];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int r = 32 * db + j;
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vbase + r * 128 + 16 * ((2 * u + hf) ^ Cfg::swz_v(r)));
+        o[db] = mfma_bf16(va, pb, o[db]);
+      }
+    }
+
+    __builtin_amdgcn_s_waitcnt(0);     // this wave's direct loads of the next tile landed
+    __syncthreads();                   // ... and every other wave's; all reads of `stage` done
+    slot = nslot;
+    b = nbk;
+    f = nf;
+  }
+
+  // ---- epilogue
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!qvalid) return;
+  if (it.split < 0) {
+    const float inv = 1.f / l_tot;
+    const size_t ooff = (size_t)(it.q_tok0 + qi) * rs + (size_t)h * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * db + 8 * g + 4 * hf;
+        const uint2 pk = make_uint2(pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
+                                    pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.O) + ooff + dd) = pk;
+      }
+  } else {
+    const int n = it.q_tok0 - (it.anchor_idx == 0 ? 0 : (F - 1) * N) + qi;
+    const size_t row = (((size_t)it.split * H + h) * a.na + it.anchor_idx) * N + n;
+    float* po = a.part_O + row * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * db + 8 * g + 4 * hf;
+        *reinterpret_cast<float4*>(po + dd) =
+            make_float4(o[db][4 * g + 0], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+      }
+    if (hf == 0) {
+      a.part_ml[2 * row + 0] = m_run;
+      a.part_ml[2 * row + 1] = l_tot;
+    }
+  }
+}
+
 // ============================================================ combine
 // One thread per (split-merged row, 4 channels).  Rows: [H][na][N].
 template <int D, bool F32OUT>
@@ -683,21 +982,30 @@ void attn_split_plan(int F, int* nsplit, int* fs) {
   *nsplit = (F + f - 1) / f;
 }
 
-template <int D, int PREC>
-static hipError_t attn_d(AttnArgs a, hipStream_t st) {
-  using Cfg = AttnCfg<D, PREC>;
-  const int lds = 2 * Cfg::STAGE;
-  static bool attr_done = false;     // benign race: the attribute value is the same
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<D, PREC>),
+template <typename KernelFn>
+static hipError_t attn_launch(KernelFn fn, int lds, bool* attr_done, const AttnArgs& a, hipStream_t st) {
+  if (!*attr_done) {     // benign race: every caller sets the same value
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    attr_done = true;
+    *attr_done = true;
   }
   const int nitems = a.n_anchor_items + a.H * a.tiles_per_head;
   if (nitems == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_kernel<D, PREC>), dim3(nitems), dim3(256), lds, st, a);
+  hipLaunchKernelGGL(fn, dim3(nitems), dim3(256), lds, st, a);
   return hipGetLastError();
+}
+
+// fp32 I/O: the register-staged kernel; bf16 and fp8: the direct-to-LDS kernel
+template <int D>
+static hipError_t attn_f32(const AttnArgs& a, hipStream_t st) {
+  static bool done = false;
+  return attn_launch(&attn_kernel<D, 0>, 2 * AttnCfg<D, 0>::STAGE, &done, a, st);
+}
+template <int D, int PREC>
+static hipError_t attn_lds(const AttnArgs& a, hipStream_t st) {
+  static bool done = false;
+  return attn_launch(&attn_lds_kernel<D, PREC>, 2 * LdsCfg<D, PREC>::STAGE, &done, a, st);
 }
 
 hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, const uint16_t* vt,
@@ -718,12 +1026,18 @@ hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, co
   }
   a.tiles_per_head = tph;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-#define VDN_ATTN_CASE(DD, PP) \
-  if (D == DD && prec == PP) return attn_d<DD, PP>(a, st);
-  VDN_ATTN_CASE(32, 0) VDN_ATTN_CASE(64, 0) VDN_ATTN_CASE(128, 0)
-  VDN_ATTN_CASE(32, 1) VDN_ATTN_CASE(64, 1) VDN_ATTN_CASE(128, 1)
-  VDN_ATTN_CASE(64, 2) VDN_ATTN_CASE(128, 2)
-#undef VDN_ATTN_CASE
+  if (prec == 0) {
+    if (D == 32) return attn_f32<32>(a, st);
+    if (D == 64) return attn_f32<64>(a, st);
+    if (D == 128) return attn_f32<128>(a, st);
+  } else if (prec == 1) {
+    if (D == 32) return attn_lds<32, 1>(a, st);
+    if (D == 64) return attn_lds<64, 1>(a, st);
+    if (D == 128) return attn_lds<128, 1>(a, st);
+  } else if (prec == 2) {
+    if (D == 64) return attn_lds<64, 2>(a, st);
+    if (D == 128) return attn_lds<128, 2>(a, st);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -16,6 +16,10 @@ typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef int intx4 __attribute__((ext_vector_type(4)));
 typedef int intx2 __attribute__((ext_vector_type(2)));
 
+// LDS (address space 3) pointer, as the direct global->LDS load builtin takes it;
+// convert from a generic pointer into __shared__ memory with an explicit cast
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
 constexpr int kChunk = 5;        // latent frames per chunk
 constexpr int kWave = 64;
 
