@@ -561,6 +561,12 @@ struct LdsCfg {
   __device__ static int swz_v(int r) { return r & 7; }
 };
 
+template <int KX, int VX>
+struct LaneOffsets {
+  uint32_t koff[KX], voff[VX];
+  int krow[KX], kchk[KX];
+};
+
 struct Item {
   int h, q_tok0, q_rows, split, anchor_idx;
   int mode;          // 0: frames [k_f0, k_f0 + nslots); 1: chunk key list
@@ -665,29 +671,47 @@ __global__ __launch_bounds__(256, 2) void attn_lds_kernel(AttnArgs a) {
   auto frame_of = [&](int slot) {
     return it.mode == 0 ? it.k_f0 + slot : chunk_key_frame(slot, it.wf, it.we, F);
   };
+  // Per-lane byte offsets of this lane's 16-byte pieces inside a K tile (rows of
+  // the token-major k tensor) and a V^T block; the tile base is wave-uniform.
+  // (Kept in a struct: clang drops the host launch stub of a kernel template
+  // whose lambda captures local arrays sized by a dependent constant.)
+  constexpr int KX = Cfg::K_INSTR / 4, VX = Cfg::V_INSTR / 4;
+  const size_t krs = rs * (FP8 ? 1 : 2);             // token stride in bytes
+  LaneOffsets<KX, VX> lo;
+  uint32_t* koff = lo.koff;
+  uint32_t* voff = lo.voff;
+  int* krow = lo.krow;
+  int* kchk = lo.kchk;
+#pragma unroll
+  for (int x = 0; x < KX; ++x) {
+    const int ii = w * KX + x;
+    krow[x] = ii * Cfg::K_RPI + lane / Cfg::KCH;
+    kchk[x] = (lane % Cfg::KCH) ^ Cfg::swz_k(krow[x]);
+    koff[x] = (uint32_t)(krow[x] * krs) + 16u * kchk[x];
+  }
+#pragma unroll
+  for (int x = 0; x < VX; ++x) {
+    const int ii = w * VX + x;
+    const int r = ii * 8 + (lane >> 3);
+    voff[x] = (uint32_t)(r * 128 + 16 * ((lane & 7) ^ Cfg::swz_v(r)));
+  }
   auto issue_tile = [&](int stage, int f, int b) {
     unsigned char* sbase = smem + stage * Cfg::STAGE;
     const int nvalid = min(BK, N - BK * b);
-    const size_t tok0 = (size_t)f * N + BK * b;
+    const unsigned char* kt = kbase + (((size_t)f * N + BK * b) * rs + (size_t)h * D) * (FP8 ? 1 : 2);
 #pragma unroll
-    for (int x = 0; x < Cfg::K_INSTR / 4; ++x) {
-      const int ii = w * (Cfg::K_INSTR / 4) + x;
-      const int r = ii * Cfg::K_RPI + lane / Cfg::KCH;
-      const int c = (lane % Cfg::KCH) ^ Cfg::swz_k(r);
-      const int n = min(r, nvalid - 1);               // rows past the frame: any valid row
-      const unsigned char* src = kbase + ((tok0 + n) * rs + (size_t)h * D) * (FP8 ? 1 : 2) + 16 * c;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)(sbase + 1024 * ii), 16, 0, 0);
+    for (int x = 0; x < KX; ++x) {
+      // rows past the frame's end re-read its last row (their scores are masked)
+      const uint32_t off = nvalid == BK ? koff[x]
+                                        : (uint32_t)(min(krow[x], nvalid - 1) * krs) + 16u * kchk[x];
+      __builtin_amdgcn_global_load_lds(kt + off, (lds_void_ptr)(sbase + 1024 * (w * KX + x)), 16, 0, 0);
     }
     const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(
         a.vt + (((size_t)h * F + f) * nb + b) * (size_t)(D * BK));
 #pragma unroll
-    for (int x = 0; x < Cfg::V_INSTR / 4; ++x) {
-      const int ii = w * (Cfg::V_INSTR / 4) + x;
-      const int r = ii * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ Cfg::swz_v(r);
-      __builtin_amdgcn_global_load_lds(vsrc + r * 128 + 16 * c,
-                                       (lds_void_ptr)(sbase + Cfg::K_BYTES + 1024 * ii), 16, 0, 0);
-    }
+    for (int x = 0; x < VX; ++x)
+      __builtin_amdgcn_global_load_lds(vsrc + voff[x],
+                                       (lds_void_ptr)(sbase + Cfg::K_BYTES + 1024 * (w * VX + x)), 16, 0, 0);
   };
 
   floatx16 o[NDB];
@@ -767,19 +791,16 @@ __global__ __launch_bounds__(256, 2) void attn_lds_kernel(AttnArgs a) {
       for (int x = 0; x < NDB; ++x) o[x] *= alpha;
     }
     const float neg_m = -m_run;
-    float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale, neg_m));
-        s[kb][r] = p;
-        psum += p;
-      }
-    l_run += psum;
+      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale, neg_m));
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T; the row sum l takes the same bf16 P values, two per
+    // v_dot2_f32_bf16 against (1, 1)
     const unsigned char* vbase = sbase + Cfg::K_BYTES;
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    float psum = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int kb = u >> 1, e0 = 8 * (u & 1);
@@ -787,12 +808,16 @@ __global__ __launch_bounds__(256, 2) void attn_lds_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[kb][e0 + e];
 #pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[e], pb[e + 1]}, ones, psum, false);
+#pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int r = 32 * db + j;
         const bf16x8 va = *reinterpret_cast<const bf16x8*>(vbase + r * 128 + 16 * ((2 * u + hf) ^ Cfg::swz_v(r)));
         o[db] = mfma_bf16(va, pb, o[db]);
       }
     }
+    l_run += psum;
 
     __builtin_amdgcn_s_waitcnt(0);     // this wave's direct loads of the next tile landed
     __syncthreads();                   // ... and every other wave's; all reads of `stage` done
