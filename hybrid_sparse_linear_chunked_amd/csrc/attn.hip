@@ -17,6 +17,8 @@
 //                    softmax in fp32 registers, 32x32 MFMA for Q.K^T and P.V.
 //   combine_kernel   log-sum-exp merge of the anchor rows' key slices.
 //   amax / quant     per-head E4M3 quantiser of the fp8 Q.K^T variant.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -153,10 +155,18 @@ struct AttnArgs {
   int nsplit, fs, na, qt_anchor;
   int n_anchor_items;
   int tiles_per_head;     // sum over chunks of the chunk items' tile counts
+  int bq;                 // query rows per work item (32 per wave)
   float scale_log2;       // log2(e) / sqrt(D)
 };
 
-constexpr int BQ = 128;   // queries per work item (4 waves x 32)
+constexpr int BQ = 128;   // queries per work item of attn_kernel (4 waves x 32)
+#ifndef VDN_LDS_WAVES
+#define VDN_LDS_WAVES 8
+#endif
+constexpr int kLdsWaves = VDN_LDS_WAVES;   // waves per workgroup of attn_lds_kernel
+#ifndef VDN_LDS_WAITALL
+#define VDN_LDS_WAITALL 0    // 1: wait for all LDS reads before issuing each operand batch
+#endif
 constexpr int BK = 64;    // keys per tile
 constexpr float kLazy = 8.f;   // log2 headroom before the running max is raised
 
@@ -228,8 +238,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     split = r % a.nsplit;
     h = r / a.nsplit;
     const int qf = anchor_idx == 0 ? 0 : F - 1;
-    q_tok0 = qf * N + qt * BQ;
-    q_rows = min(BQ, N - qt * BQ);
+    q_tok0 = qf * N + qt * a.bq;
+    q_rows = min(a.bq, N - qt * a.bq);
     kf_mode = 0;
     k_f0 = split * a.fs;
     k_f1 = min(F, k_f0 + a.fs);
@@ -242,13 +252,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     int c = 0;
     for (; c < C; ++c) {
       const int nf = nq_end(c, F) - nq_first(c);
-      const int t = nf > 0 ? (nf * N + BQ - 1) / BQ : 0;
+      const int t = nf > 0 ? (nf * N + a.bq - 1) / a.bq : 0;
       if (r < t) break;
       r -= t;
     }
     const int tok_begin = nq_first(c) * N, tok_end = nq_end(c, F) * N;
-    q_tok0 = tok_begin + r * BQ;
-    q_rows = min(BQ, tok_end - q_tok0);
+    q_tok0 = tok_begin + r * a.bq;
+    q_rows = min(a.bq, tok_end - q_tok0);
     kf_mode = 1;
     wf = win_first(c);
     we = win_end(c, F);
@@ -538,11 +548,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 
 // ============================================================ attention, bf16 / fp8
 // Same work items and arithmetic as attn_kernel, with K and V^T tiles moved
-// global -> LDS by the 16-byte direct loads of gfx950 (global_load_lds_dwordx4):
-// no staging registers, no LDS store instructions.  A direct load writes the 64
-// lanes' 16-byte pieces to 1 KiB of consecutive LDS, so bank conflicts are
-// avoided with an XOR swizzle of the 16-byte chunks inside a row instead of row
-// padding: chunk c of row r sits at position c ^ swz(r).
+// global -> LDS by the 16-byte direct loads of gfx950 (buffer_load_dwordx4 ...
+// lds): no staging registers, no LDS store instructions.  A direct load writes
+// the 64 lanes' 16-byte pieces to 1 KiB of consecutive LDS, so bank conflicts
+// are avoided with an XOR swizzle of the 16-byte chunks inside a row instead of
+// row padding: chunk c of row r sits at position c ^ swz(r).
 template <int D, int PREC>
 struct LdsCfg {
   static constexpr bool FP8 = PREC == 2;
@@ -555,11 +565,49 @@ struct LdsCfg {
   static constexpr int V_INSTR = V_BYTES / 1024;
   static constexpr int K_RPI = 1024 / KROW;        // K rows per direct load
   static constexpr int QSTEPS = FP8 ? D / 64 : D / 16;
-  static_assert(K_INSTR % 4 == 0 && V_INSTR % 4 == 0, "tiles split over 4 waves");
-  // 8 consecutive rows must land on distinct 16-byte bank groups
-  __device__ static int swz_k(int r) { return KROW >= 128 ? (r & 7) : ((r >> 1) & 3); }
-  __device__ static int swz_v(int r) { return r & 7; }
+  static_assert(K_INSTR >= 1 && V_INSTR >= 1, "a tile is at least one wave-wide load");
+  // gfx950's LDS serves 256 bytes (64 banks x 4 B) per cycle, i.e. 16 lanes of a
+  // ds_read_b128; the 16 rows read by those lanes must cover 16 distinct 16-byte
+  // bank groups.  A row of `bytes` bytes starts at bank group (r * bytes / 16) % 16,
+  // so rows sharing a start group are told apart by XOR-ing their chunk index.
+  __device__ static int swz_rows(int r, int bytes) {
+    const int rpb = bytes >= 256 ? 1 : 256 / bytes;    // rows per 256-byte bank cycle
+    const int nch = bytes / 16 < 16 ? bytes / 16 : 16;
+    return (r / rpb) & (nch - 1);
+  }
+  __device__ static int swz_k(int r) { return swz_rows(r, KROW); }
+  __device__ static int swz_v(int r) { return swz_rows(r, 128); }
+  // LDS operand of one Q.K^T MFMA: K rows 32*kb + (lane & 31), reduction step
+  // st, for item i = 2*st + kb (bf16: 16 dims; fp8: 64 dims)
+  using KFrag = typename std::conditional<FP8, intx8, bf16x8>::type;
+  __device__ static KFrag kfrag(const unsigned char* sbase, int i, int j, int hf) {
+    const int st = i >> 1, kb = i & 1;
+    const int r = 32 * kb + j;
+    const unsigned char* krow = sbase + r * KROW;
+    const int sw = swz_k(r);
+    if constexpr (FP8) {
+      const int c0 = 4 * st + 2 * hf;
+      const uint4 x0 = *reinterpret_cast<const uint4*>(krow + 16 * (c0 ^ sw));
+      const uint4 x1 = *reinterpret_cast<const uint4*>(krow + 16 * ((c0 + 1) ^ sw));
+      return KFrag{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    } else {
+      return *reinterpret_cast<const bf16x8*>(krow + 16 * ((2 * st + hf) ^ sw));
+    }
+  }
+  // LDS operand of one P.V MFMA: V^T rows 32*db + (lane & 31), keys 16u..16u+15
+  __device__ static bf16x8 vfrag(const unsigned char* vbase, int u, int db, int j, int hf) {
+    const int r = 32 * db + j;
+    return *reinterpret_cast<const bf16x8*>(vbase + r * 128 + 16 * ((2 * u + hf) ^ swz_v(r)));
+  }
 };
+
+// Buffer resource for raw byte-offset loads of `bytes` bytes from `base` (gfx9
+// word 3: 32-bit data format, no swizzle); offsets past `bytes` read zeros.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
+__device__ inline void lds_wait_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 template <int KX, int VX>
 struct LaneOffsets {
@@ -593,8 +641,8 @@ __device__ inline Item decode_item(const AttnArgs& a) {
     it.split = r % a.nsplit;
     it.h = r / a.nsplit;
     const int qf = it.anchor_idx == 0 ? 0 : F - 1;
-    it.q_tok0 = qf * N + qt * BQ;
-    it.q_rows = min(BQ, N - qt * BQ);
+    it.q_tok0 = qf * N + qt * a.bq;
+    it.q_rows = min(a.bq, N - qt * a.bq);
     it.mode = 0;
     it.k_f0 = it.split * a.fs;
     it.nslots = min(F, it.k_f0 + a.fs) - it.k_f0;
@@ -608,13 +656,13 @@ __device__ inline Item decode_item(const AttnArgs& a) {
     int c = 0;
     for (; c < C; ++c) {
       const int nf = nq_end(c, F) - nq_first(c);
-      const int t = nf > 0 ? (nf * N + BQ - 1) / BQ : 0;
+      const int t = nf > 0 ? (nf * N + a.bq - 1) / a.bq : 0;
       if (r < t) break;
       r -= t;
     }
     const int tok_begin = nq_first(c) * N, tok_end = nq_end(c, F) * N;
-    it.q_tok0 = tok_begin + r * BQ;
-    it.q_rows = min(BQ, tok_end - it.q_tok0);
+    it.q_tok0 = tok_begin + r * a.bq;
+    it.q_rows = min(a.bq, tok_end - it.q_tok0);
     it.mode = 1;
     it.wf = win_first(c);
     it.we = win_end(c, F);
@@ -623,19 +671,36 @@ __device__ inline Item decode_item(const AttnArgs& a) {
   return it;
 }
 
-template <int D, int PREC>
-__global__ __launch_bounds__(256, 2) void attn_lds_kernel(AttnArgs a) {
+// An item with every field read from the first lane: it is the same in every
+// lane, and this lets the compiler keep it and what derives from it in SGPRs.
+__device__ inline Item uniform_item(Item it) {
+  it.h = __builtin_amdgcn_readfirstlane(it.h);
+  it.q_tok0 = __builtin_amdgcn_readfirstlane(it.q_tok0);
+  it.q_rows = __builtin_amdgcn_readfirstlane(it.q_rows);
+  it.split = __builtin_amdgcn_readfirstlane(it.split);
+  it.anchor_idx = __builtin_amdgcn_readfirstlane(it.anchor_idx);
+  it.mode = __builtin_amdgcn_readfirstlane(it.mode);
+  it.k_f0 = __builtin_amdgcn_readfirstlane(it.k_f0);
+  it.wf = __builtin_amdgcn_readfirstlane(it.wf);
+  it.we = __builtin_amdgcn_readfirstlane(it.we);
+  it.nslots = __builtin_amdgcn_readfirstlane(it.nslots);
+  return it;
+}
+
+template <int D, int PREC, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   using Cfg = LdsCfg<D, PREC>;
   constexpr bool FP8 = Cfg::FP8;
   constexpr int NDB = D / 32;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, hf = lane >> 5;
   const int F = a.F, N = a.N, H = a.H;
   const size_t rs = (size_t)H * D;                 // token stride in elements
   const int nb = (N + BK - 1) / BK;
-  const Item it = decode_item(a);
+  // the item is wave-uniform; say so, so that tile bookkeeping stays in SGPRs
+  const Item it = uniform_item(decode_item(a));
   const int h = it.h;
   const int ntiles = it.nslots * nb;
 
@@ -665,7 +730,7 @@ __global__ __launch_bounds__(256, 2) void attn_lds_kernel(AttnArgs a) {
   float scale = a.scale_log2;
   if constexpr (FP8) scale *= (a.amax[h] * (1.f / 448.f)) * (a.amax[H + h] * (1.f / 448.f));
 
-  // ---- direct global -> LDS tile loads
+  // ---- global -> LDS tile loads
   const unsigned char* kbase = FP8 ? reinterpret_cast<const unsigned char*>(a.k8)
                                    : static_cast<const unsigned char*>(a.k);
   auto frame_of = [&](int slot) {
@@ -675,7 +740,9 @@ __global__ __launch_bounds__(256, 2) void attn_lds_kernel(AttnArgs a) {
   // the token-major k tensor) and a V^T block; the tile base is wave-uniform.
   // (Kept in a struct: clang drops the host launch stub of a kernel template
   // whose lambda captures local arrays sized by a dependent constant.)
-  constexpr int KX = Cfg::K_INSTR / 4, VX = Cfg::V_INSTR / 4;
+  // every wave issues KX of the tile's K loads and VX of its V loads (the last
+  // waves fewer when the count does not divide)
+  constexpr int KX = (Cfg::K_INSTR + NW - 1) / NW, VX = (Cfg::V_INSTR + NW - 1) / NW;
   const size_t krs = rs * (FP8 ? 1 : 2);             // token stride in bytes
   LaneOffsets<KX, VX> lo;
   uint32_t* koff = lo.koff;
@@ -695,24 +762,36 @@ __global__ __launch_bounds__(256, 2) void attn_lds_kernel(AttnArgs a) {
     const int r = ii * 8 + (lane >> 3);
     voff[x] = (uint32_t)(r * 128 + 16 * ((lane & 7) ^ Cfg::swz_v(r)));
   }
-  auto issue_tile = [&](int stage, int f, int b) {
+  // loads [x0, x1) of this wave's share of a tile: K loads first, then V^T loads
+  constexpr int LPT = KX + VX;
+  auto issue_range = [&](int stage, int f, int b, int x0, int x1) {
     unsigned char* sbase = smem + stage * Cfg::STAGE;
     const int nvalid = min(BK, N - BK * b);
+    // buffer loads to LDS (MUBUF): unlike the FLAT-encoded global_load_lds they
+    // leave the compiler free to wait for LDS reads one by one (lgkmcnt(n))
     const unsigned char* kt = kbase + (((size_t)f * N + BK * b) * rs + (size_t)h * D) * (FP8 ? 1 : 2);
+    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kt, (uint32_t)(BK * krs));
 #pragma unroll
     for (int x = 0; x < KX; ++x) {
+      if (x < x0 || x >= x1) continue;
+      if (Cfg::K_INSTR % NW != 0 && w * KX + x >= Cfg::K_INSTR) break;
       // rows past the frame's end re-read its last row (their scores are masked)
       const uint32_t off = nvalid == BK ? koff[x]
                                         : (uint32_t)(min(krow[x], nvalid - 1) * krs) + 16u * kchk[x];
-      __builtin_amdgcn_global_load_lds(kt + off, (lds_void_ptr)(sbase + 1024 * (w * KX + x)), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_ptr)(sbase + 1024 * (w * KX + x)), 16, off, 0, 0, 0);
     }
     const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(
         a.vt + (((size_t)h * F + f) * nb + b) * (size_t)(D * BK));
+    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vsrc, (uint32_t)(D * BK * 2));
 #pragma unroll
-    for (int x = 0; x < VX; ++x)
-      __builtin_amdgcn_global_load_lds(vsrc + voff[x],
-                                       (lds_void_ptr)(sbase + Cfg::K_BYTES + 1024 * (w * VX + x)), 16, 0, 0);
+    for (int x = 0; x < VX; ++x) {
+      if (KX + x < x0 || KX + x >= x1) continue;
+      if (Cfg::V_INSTR % NW != 0 && w * VX + x >= Cfg::V_INSTR) break;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void_ptr)(sbase + Cfg::K_BYTES + 1024 * (w * VX + x)), 16,
+                                               voff[x], 0, 0, 0);
+    }
   };
+  auto issue_tile = [&](int stage, int f, int b) { issue_range(stage, f, b, 0, LPT); };
 
   floatx16 o[NDB];
 #pragma unroll
@@ -734,38 +813,45 @@ __global__ __launch_bounds__(256, 2) void attn_lds_kernel(AttnArgs a) {
     int nf = f;
     if (t + 1 < ntiles) {
       nf = nbk == 0 ? frame_of(nslot) : f;
-      issue_tile(stage ^ 1, nf, nbk);
     }
     const int nvalid = min(BK, N - BK * b);
     const unsigned char* sbase = smem + stage * Cfg::STAGE;
 
-    // ---- S^T = K Q^T for two 32-key blocks
-    floatx16 s[2];
+    // ---- S^T = K Q^T.  Operand fragments come from LDS in batches, double
+    // buffered: each batch's reads are issued before the previous batch's
+    // MFMAs, so one batch is in flight while the matrix core works.
+    const unsigned char* vbase = sbase + Cfg::K_BYTES;
+    constexpr int NQK = 2 * Cfg::QSTEPS, QB = NQK < 4 ? NQK : 4, NQB = NQK / QB;
+    typename LdsCfg<D, PREC>::KFrag kf[2][QB];
+    bf16x8 va[2][NDB];
+    floatx16 s[2] = {floatx16{}, floatx16{}};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = floatx16{};
-      const int r = 32 * kb + j;
-      const unsigned char* krow = sbase + r * Cfg::KROW;
-      const int sw = Cfg::swz_k(r);
-      if constexpr (FP8) {
+    for (int x = 0; x < QB; ++x) kf[0][x] = Cfg::kfrag(sbase, x, j, hf);
 #pragma unroll
-        for (int st = 0; st < Cfg::QSTEPS; ++st) {
-          const int c0 = 4 * st + 2 * hf;
-          const uint4 x0 = *reinterpret_cast<const uint4*>(krow + 16 * (c0 ^ sw));
-          const uint4 x1 = *reinterpret_cast<const uint4*>(krow + 16 * ((c0 + 1) ^ sw));
-          const intx8 ka = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-          s[kb] = mfma_fp8(ka, q8f[st], s[kb]);
-        }
+    for (int bt = 0; bt < NQB; ++bt) {
+      if (VDN_LDS_WAITALL) lds_wait_all();
+      if (bt + 1 < NQB) {
+#pragma unroll
+        for (int x = 0; x < QB; ++x) kf[(bt + 1) & 1][x] = Cfg::kfrag(sbase, (bt + 1) * QB + x, j, hf);
       } else {
 #pragma unroll
-        for (int st = 0; st < Cfg::QSTEPS; ++st) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 16 * ((2 * st + hf) ^ sw));
-          s[kb] = mfma_bf16(ka, qb[st], s[kb]);
-        }
+        for (int db = 0; db < NDB; ++db) va[0][db] = Cfg::vfrag(vbase, 0, db, j, hf);
       }
+      // this batch's share of the next tile's loads: spread over the batches so
+      // the address unit works through them while the MFMAs run, instead of
+      // every wave queueing its loads at once
+      if (t + 1 < ntiles) issue_range(stage ^ 1, nf, nbk, bt * LPT / NQB, (bt + 1) * LPT / NQB);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int x = 0; x < QB; ++x) {
+        const int i = bt * QB + x, st = i >> 1, kb = i & 1;
+        if constexpr (FP8) s[kb] = mfma_fp8(kf[bt & 1][x], q8f[st], s[kb]);
+        else s[kb] = mfma_bf16(kf[bt & 1][x], qb[st], s[kb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- online softmax (see attn_kernel)
+    // ---- online softmax (see attn_kernel): maxima, lazy raise
     if (nvalid < BK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -775,11 +861,9 @@ __global__ __launch_bounds__(256, 2) void attn_lds_kernel(AttnArgs a) {
           if (key >= nvalid) s[kb][r] = -INFINITY;
         }
     }
-    float mx = s[0][0];
+    float mx = __builtin_fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int e = 1; e < 31; e += 2)
-      mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[e >> 4][e & 15]), s[(e + 1) >> 4][(e + 1) & 15]);
-    mx = __builtin_fmaxf(mx, s[1][15]);
+    for (int e = 1; e < 16; ++e) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[0][e]), s[1][e]);
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
     const float mt = mx * scale;
     if (__any(mt > m_run + kLazy)) {
@@ -791,35 +875,39 @@ __global__ __launch_bounds__(256, 2) void attn_lds_kernel(AttnArgs a) {
       for (int x = 0; x < NDB; ++x) o[x] *= alpha;
     }
     const float neg_m = -m_run;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale, neg_m));
 
-    // ---- O^T += V^T P^T; the row sum l takes the same bf16 P values, two per
-    // v_dot2_f32_bf16 against (1, 1)
-    const unsigned char* vbase = sbase + Cfg::K_BYTES;
+    // ---- O^T += V^T P^T, one group of 16 keys per batch; the probabilities of
+    // the next group are formed on the VALU while this group's MFMAs run, and
+    // the row sum l takes the same bf16 values, two per v_dot2_f32_bf16
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
     float psum = 0.f;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[0][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[0][e], scale, neg_m));
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int kb = u >> 1, e0 = 8 * (u & 1);
-      bf16x8 pb;
+      if (VDN_LDS_WAITALL) lds_wait_all();
+      if (u + 1 < 4) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[kb][e0 + e];
+        for (int db = 0; db < NDB; ++db) va[(u + 1) & 1][db] = Cfg::vfrag(vbase, u + 1, db, j, hf);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] = mfma_bf16(va[u & 1][db], pb[u & 1], o[db]);
+      if (u + 1 < 4) {
+        const int kb = (u + 1) >> 1, e0 = 8 * ((u + 1) & 1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pb[(u + 1) & 1][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][e0 + e], scale, neg_m));
+      }
 #pragma unroll
       for (int e = 0; e < 8; e += 2)
-        psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[e], pb[e + 1]}, ones, psum, false);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int r = 32 * db + j;
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vbase + r * 128 + 16 * ((2 * u + hf) ^ Cfg::swz_v(r)));
-        o[db] = mfma_bf16(va, pb, o[db]);
-      }
+        psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[u & 1][e], pb[u & 1][e + 1]}, ones, psum, false);
+      __builtin_amdgcn_sched_barrier(0);
     }
     l_run += psum;
 
-    __builtin_amdgcn_s_waitcnt(0);     // this wave's direct loads of the next tile landed
+    __builtin_amdgcn_s_waitcnt(0);     // this wave's loads of the next tile landed
     __syncthreads();                   // ... and every other wave's; all reads of `stage` done
     slot = nslot;
     b = nbk;
@@ -1007,8 +1095,23 @@ void attn_split_plan(int F, int* nsplit, int* fs) {
   *nsplit = (F + f - 1) / f;
 }
 
+// work-item counts for query tiles of a.bq rows
+static void attn_items(AttnArgs& a) {
+  a.qt_anchor = (a.N + a.bq - 1) / a.bq;
+  a.n_anchor_items = a.H * a.na * a.qt_anchor * a.nsplit;
+  int tph = 0;
+  for (int c = 0; c < num_chunks(a.F); ++c) {
+    const int nf = nq_end(c, a.F) - nq_first(c);
+    if (nf > 0) tph += (int)(((long long)nf * a.N + a.bq - 1) / a.bq);
+  }
+  a.tiles_per_head = tph;
+}
+
 template <typename KernelFn>
-static hipError_t attn_launch(KernelFn fn, int lds, bool* attr_done, const AttnArgs& a, hipStream_t st) {
+static hipError_t attn_launch(KernelFn fn, int lds, bool* attr_done, AttnArgs a, hipStream_t st,
+                              int threads, int bq = 0) {
+  a.bq = bq > 0 ? bq : 32 * (threads / 64);
+  attn_items(a);
   if (!*attr_done) {     // benign race: every caller sets the same value
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -1017,7 +1120,7 @@ static hipError_t attn_launch(KernelFn fn, int lds, bool* attr_done, const AttnA
   }
   const int nitems = a.n_anchor_items + a.H * a.tiles_per_head;
   if (nitems == 0) return hipSuccess;
-  hipLaunchKernelGGL(fn, dim3(nitems), dim3(256), lds, st, a);
+  hipLaunchKernelGGL(fn, dim3(nitems), dim3(threads), lds, st, a);
   return hipGetLastError();
 }
 
@@ -1025,12 +1128,13 @@ static hipError_t attn_launch(KernelFn fn, int lds, bool* attr_done, const AttnA
 template <int D>
 static hipError_t attn_f32(const AttnArgs& a, hipStream_t st) {
   static bool done = false;
-  return attn_launch(&attn_kernel<D, 0>, 2 * AttnCfg<D, 0>::STAGE, &done, a, st);
+  return attn_launch(&attn_kernel<D, 0>, 2 * AttnCfg<D, 0>::STAGE, &done, a, st, 256);
 }
 template <int D, int PREC>
 static hipError_t attn_lds(const AttnArgs& a, hipStream_t st) {
   static bool done = false;
-  return attn_launch(&attn_lds_kernel<D, PREC>, 2 * LdsCfg<D, PREC>::STAGE, &done, a, st);
+  return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves>, 2 * LdsCfg<D, PREC>::STAGE, &done, a, st,
+                     64 * kLdsWaves);
 }
 
 hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, const uint16_t* vt,
@@ -1042,14 +1146,6 @@ hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, co
   a.F = F; a.N = N; a.H = H;
   attn_split_plan(F, &a.nsplit, &a.fs);
   a.na = F >= 2 ? 2 : 1;
-  a.qt_anchor = (N + BQ - 1) / BQ;
-  a.n_anchor_items = H * a.na * a.qt_anchor * a.nsplit;
-  int tph = 0;
-  for (int c = 0; c < num_chunks(F); ++c) {
-    const int nf = nq_end(c, F) - nq_first(c);
-    if (nf > 0) tph += (int)(((long long)nf * N + BQ - 1) / BQ);
-  }
-  a.tiles_per_head = tph;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   if (prec == 0) {
     if (D == 32) return attn_f32<32>(a, st);
