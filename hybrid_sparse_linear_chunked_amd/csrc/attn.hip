@@ -164,6 +164,10 @@ constexpr int BQ = 128;   // queries per work item of attn_kernel (4 waves x 32)
 #define VDN_LDS_WAVES 8
 #endif
 constexpr int kLdsWaves = VDN_LDS_WAVES;   // waves per workgroup of attn_lds_kernel
+#ifndef VDN_LDS_STAGES
+#define VDN_LDS_STAGES 2
+#endif
+constexpr int kLdsStages = VDN_LDS_STAGES;  // LDS tile stages of attn_lds_kernel (2 or 4)
 #ifndef VDN_LDS_WAITALL
 #define VDN_LDS_WAITALL 0    // 1: wait for all LDS reads before issuing each operand batch
 #endif
@@ -791,30 +795,42 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
                                                voff[x], 0, 0, 0);
     }
   };
-  auto issue_tile = [&](int stage, int f, int b) { issue_range(stage, f, b, 0, LPT); };
+  // Tile cursors: ld_* is the next tile to load, b the 64-key block of tile t.
+  // Tiles go through NSTG LDS stages and are loaded NSTG/2 tiles ahead; a
+  // workgroup barrier every NSTG/2 tiles publishes the loads of the next group
+  // of tiles and frees the stages of the previous one.
+  constexpr int NSTG = kLdsStages, AHEAD = NSTG / 2;
+  int ld_slot = 0, ld_b = 0, ld_f = frame_of(0);
+  auto next_load = [&]() {
+    if (++ld_b == nb) {
+      ld_b = 0;
+      ld_f = frame_of(++ld_slot);
+    }
+  };
 
   floatx16 o[NDB];
 #pragma unroll
   for (int x = 0; x < NDB; ++x) o[x] = floatx16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  int slot = 0, b = 0, f = frame_of(0);
-  issue_tile(0, f, b);
+#pragma unroll
+  for (int x = 0; x < AHEAD; ++x) {
+    if (x < ntiles) {
+      issue_range(x, ld_f, ld_b, 0, LPT);
+      next_load();
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  int b = 0;
   for (int t = 0; t < ntiles; ++t) {
-    const int stage = t & 1;
-    int nslot = slot, nbk = b + 1;
-    if (nbk == nb) {
-      nbk = 0;
-      ++nslot;
-    }
-    int nf = f;
-    if (t + 1 < ntiles) {
-      nf = nbk == 0 ? frame_of(nslot) : f;
-    }
+    const int stage = t & (NSTG - 1);
+    const bool ld = t + AHEAD < ntiles;      // load tile t + AHEAD during this tile
+    const int ldf = ld_f, ldb = ld_b;
+    if (ld) next_load();
     const int nvalid = min(BK, N - BK * b);
+    if (++b == nb) b = 0;
     const unsigned char* sbase = smem + stage * Cfg::STAGE;
 
     // ---- S^T = K Q^T.  Operand fragments come from LDS in batches, double
@@ -840,7 +856,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       // this batch's share of the next tile's loads: spread over the batches so
       // the address unit works through them while the MFMAs run, instead of
       // every wave queueing its loads at once
-      if (t + 1 < ntiles) issue_range(stage ^ 1, nf, nbk, bt * LPT / NQB, (bt + 1) * LPT / NQB);
+      if (ld) issue_range((t + AHEAD) & (NSTG - 1), ldf, ldb, bt * LPT / NQB, (bt + 1) * LPT / NQB);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int x = 0; x < QB; ++x) {
@@ -907,11 +923,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
     }
     l_run += psum;
 
-    __builtin_amdgcn_s_waitcnt(0);     // this wave's loads of the next tile landed
-    __syncthreads();                   // ... and every other wave's; all reads of `stage` done
-    slot = nslot;
-    b = nbk;
-    f = nf;
+    if ((t & (AHEAD - 1)) == AHEAD - 1 || t + 1 == ntiles) {
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next tiles landed
+      __syncthreads();                 // ... and every other wave's; all reads of this group done
+    }
   }
 
   // ---- epilogue
@@ -1133,7 +1148,7 @@ static hipError_t attn_f32(const AttnArgs& a, hipStream_t st) {
 template <int D, int PREC>
 static hipError_t attn_lds(const AttnArgs& a, hipStream_t st) {
   static bool done = false;
-  return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves>, 2 * LdsCfg<D, PREC>::STAGE, &done, a, st,
+  return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves>, kLdsStages * LdsCfg<D, PREC>::STAGE, &done, a, st,
                      64 * kLdsWaves);
 }
 
