@@ -65,6 +65,29 @@ def algorithmic_work(F, N, H, d):
                 readout_bytes=ro_bytes)
 
 
+PROFILE = {3: os.path.join(ROOT, "profiles", "attn_lds_kernel_768p_14s.txt")}
+
+
+def measured_traffic(config):
+    """HBM bytes per launch of the attention kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by its reading on a
+    copy kernel of known size), or None when there is no summary for this
+    workload or the kernel source changed after the counters were taken."""
+    import hashlib
+    path = PROFILE.get(config)
+    if not path or not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(os.path.join(ROOT, "hybrid_sparse_linear_chunked_amd", "csrc", "attn.hip"),
+                              "rb").read()).hexdigest()[:16]
+    recorded, traffic = None, None
+    for line in open(path):
+        if line.startswith("attn.hip sha256[:16] when measured:"):
+            recorded = line.rsplit(":", 1)[1].strip()
+        if line.startswith("attn_lds_kernel traffic_bytes_per_launch:"):
+            traffic = float(line.rsplit(":", 1)[1])
+    return traffic if recorded == sha else None
+
+
 def cpu_baseline(F, N, H, d, seed=0, tokens=384):
     """Time the fp64 oracle on a bounded sample of the workload and extrapolate to
     one layer (ms).  Sample: head 0; the softmax of `tokens` query tokens of one
@@ -215,8 +238,8 @@ def main():
         peak = PEAK_BF16_TFLOPS
     achieved = work["soft"] / (attn_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                "kernel": "attn_kernel", "flop_per_launch": work["soft"], "kernel_ms": round(attn_ms, 3)}
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.config),
+                "kernel": "attn_lds_kernel", "flop_per_launch": work["soft"], "kernel_ms": round(attn_ms, 3)}
     ro_ms = stages.get("readout")
     readout = None
     if ro_ms:

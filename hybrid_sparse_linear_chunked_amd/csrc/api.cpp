@@ -80,7 +80,7 @@ Layout layout(int F, int N, int H, int d, int prec) {
   L.B = take(static_cast<size_t>(F) * H * dd * 4);
   L.Sf = take(C * H * dd * 4);
   L.Sb = take(C * H * dd * 4);
-  L.W = take(C * H * dd * 4);              // bf16 hi + lo, or fp32
+  L.W = take(C * H * dd * 4);              // bf16 (first half), or fp32
   L.pO = take(static_cast<size_t>(nsplit) * H * na * N * d * 4);
   L.pml = take(static_cast<size_t>(nsplit) * H * na * N * 2 * 4);
   if (prec == VDN_PREC_BF16_FP8QK) {

@@ -570,15 +570,7 @@ struct LdsCfg {
   static constexpr int K_RPI = 1024 / KROW;        // K rows per direct load
   static constexpr int QSTEPS = FP8 ? D / 64 : D / 16;
   static_assert(K_INSTR >= 1 && V_INSTR >= 1, "a tile is at least one wave-wide load");
-  // gfx950's LDS serves 256 bytes (64 banks x 4 B) per cycle, i.e. 16 lanes of a
-  // ds_read_b128; the 16 rows read by those lanes must cover 16 distinct 16-byte
-  // bank groups.  A row of `bytes` bytes starts at bank group (r * bytes / 16) % 16,
-  // so rows sharing a start group are told apart by XOR-ing their chunk index.
-  __device__ static int swz_rows(int r, int bytes) {
-    const int rpb = bytes >= 256 ? 1 : 256 / bytes;    // rows per 256-byte bank cycle
-    const int nch = bytes / 16 < 16 ? bytes / 16 : 16;
-    return (r / rpb) & (nch - 1);
-  }
+  // chunk c of row r sits at position c ^ swz(r) (swz_rows in common.h)
   __device__ static int swz_k(int r) { return swz_rows(r, KROW); }
   __device__ static int swz_v(int r) { return swz_rows(r, 128); }
   // LDS operand of one Q.K^T MFMA: K rows 32*kb + (lane & 31), reduction step
@@ -605,11 +597,6 @@ struct LdsCfg {
   }
 };
 
-// Buffer resource for raw byte-offset loads of `bytes` bytes from `base` (gfx9
-// word 3: 32-bit data format, no swizzle); offsets past `bytes` read zeros.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 // s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
 __device__ inline void lds_wait_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 

@@ -20,6 +20,22 @@ typedef int intx2 __attribute__((ext_vector_type(2)));
 // convert from a generic pointer into __shared__ memory with an explicit cast
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+// Buffer resource for raw byte-offset loads of `bytes` bytes from `base` (gfx9
+// word 3: 32-bit data format, no swizzle); offsets past `bytes` read zeros.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16-byte chunk swizzle for rows of `bytes` bytes in LDS (64 banks x 4 B = 256 B
+// per cycle, i.e. 16 lanes of a ds_read_b128): rows that start on the same
+// 16-byte bank group get their chunk index XOR-ed with different values, so 16
+// consecutive rows read at one logical chunk hit 16 distinct bank groups.
+__device__ inline int swz_rows(int r, int bytes) {
+  const int rpb = bytes >= 256 ? 1 : 256 / bytes;    // rows per 256-byte bank cycle
+  const int nch = bytes / 16 < 16 ? bytes / 16 : 16;
+  return (r / rpb) & (nch - 1);
+}
+
 constexpr int kChunk = 5;        // latent frames per chunk
 constexpr int kWave = 64;
 

@@ -345,9 +345,9 @@ __global__ __launch_bounds__(2 * D) void scan_kernel(const float* __restrict__ M
 }
 
 // ============================================================ readout weights
-// W[c][h] = diag(g_h) (S_fwd[c][h] + S_bwd[c][h]) (g = 1 when gate is null).
-// bf16 path: stored as bf16 hi and lo parts (hi = bf16(W), lo = bf16(W - hi)) so
-// the bf16 MFMA readout keeps ~16 mantissa bits of W; fp32 path: fp32.
+// W[c][h] = diag(g_h) (S_fwd[c][h] + S_bwd[c][h]) (g = 1 when gate is null),
+// rounded to bf16 for the bf16 MFMA readout (relative error <= 2^-9 per entry);
+// fp32 path: fp32.
 __global__ void wprep_kernel(const float* __restrict__ Sf, const float* __restrict__ Sb,
                              const float* __restrict__ gate, int C, int H, int D, int bf16,
                              void* __restrict__ W) {
@@ -357,84 +357,130 @@ __global__ void wprep_kernel(const float* __restrict__ Sf, const float* __restri
     const int h = (i / ((size_t)D * D)) % H;
     const float g = gate ? gate[(size_t)h * D + dv] : 1.f;
     const float x = g * (Sf[i] + Sb[i]);
-    if (bf16) {
-      const uint16_t hi = f32_to_bf16_bits(x);
-      const uint16_t lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
-      uint16_t* Wb = static_cast<uint16_t*>(W);
-      Wb[i] = hi;
-      Wb[n + i] = lo;
-    } else {
-      static_cast<float*>(W)[i] = x;
-    }
+    if (bf16) static_cast<uint16_t*>(W)[i] = f32_to_bf16_bits(x);
+    else static_cast<float*>(W)[i] = x;
   }
 }
 
 // ============================================================ readout (bf16)
-// grid (RX, C, H), 256 threads.  Tokens of chunk c's non-anchor frames, tiles of
-// 128 (32 per wave).  O_lin^T = W q^T with W (hi and lo) resident in LDS and q as
-// the MFMA B operand; ACC: O += O_lin, else O = O_lin.
+// grid (RX, C, H), 256 threads.  Tiles of 64 tokens of chunk c's non-anchor
+// frames, the RX workgroups of a (chunk, head) striding over them.
+// O_lin^T = W q^T with W (its bf16 part) in LDS and q as the MFMA B operand; wave
+// w takes tokens 32*(w & 1) .. +32 of the tile and output rows (value dims)
+// 64*(w >> 1) .. +64.  ACC: O += O_lin, else O = O_lin.
+//
+// Global memory is touched only by whole-row accesses: the q and O tiles come in
+// by 16-byte direct loads to LDS (lane L of a load takes 16 bytes of row L/RPL),
+// and the result goes out from LDS by 16-byte stores in the same pattern.  A
+// per-lane layout that follows the MFMA operands instead spreads every 64-lane
+// access over 32 rows, which leaves the address unit, not HBM, as the limit.
+// Tile rows are 2*D bytes; 16-byte chunks are XOR-swizzled per row (swz_rows) so
+// the MFMA-order reads and writes of 16 consecutive rows hit distinct banks.
+template <int D>
+struct ReadoutCfg {
+  static constexpr int TT = 64;                 // tokens per tile
+  static constexpr int RB = 2 * D;              // bytes per token row
+  static constexpr int RPL = RB / 16;           // 16-byte pieces per row
+  static constexpr int RPI = 1024 / RB;         // rows per 1 KiB direct load
+  static constexpr int LOADS = TT / RPI;        // direct loads per tile (q or O)
+  static constexpr int P = D + 8;               // W row pitch in LDS (elements)
+  static constexpr int NAB = D / 64 > 0 ? D / 64 : 1;   // 32-row output blocks per wave
+  static constexpr int NWR = D / (32 * NAB);    // waves along the output rows
+  static_assert(NWR * 2 <= 4, "4 waves cover 2 token halves x the output rows");
+  static constexpr int TILE_BYTES = TT * RB;
+};
+
 template <int D, bool ACC>
 __global__ __launch_bounds__(256, 2) void readout_kernel(const uint16_t* __restrict__ q,
                                                       const uint16_t* __restrict__ Wb, int F,
                                                       int N, int H, uint16_t* __restrict__ O) {
-  constexpr int P = D + 8;
-  constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][D * P];
+  using Cfg = ReadoutCfg<D>;
+  constexpr int P = Cfg::P, RB = Cfg::RB, RPL = Cfg::RPL, RPI = Cfg::RPI, NAB = Cfg::NAB;
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[D * P];
+  __shared__ __attribute__((aligned(16))) unsigned char qt[Cfg::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char ot[Cfg::TILE_BYTES];
   const int c = blockIdx.y, h = blockIdx.z;
-  const int C = num_chunks(F);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, j = lane & 31, hf = lane >> 5;
   const int tok_begin = nq_first(c) * N, tok_end = nq_end(c, F) * N;
   if (tok_end <= tok_begin) return;
-  const size_t n = (size_t)C * H * D * D;
   {
     const uint16_t* src = Wb + ((size_t)c * H + h) * D * D;
-    for (int x = tid; x < 2 * D * D / 8; x += 256) {
-      const int part = x / (D * D / 8), cc = x % (D * D / 8);
-      const int r = (8 * cc) / D, col = (8 * cc) % D;
-      *reinterpret_cast<uint4*>(&Ws[part][r * P + col]) =
-          *reinterpret_cast<const uint4*>(src + part * n + 8 * cc);
+    for (int x = tid; x < D * D / 8; x += 256) {
+      const int r = (8 * x) / D, col = (8 * x) % D;
+      *reinterpret_cast<uint4*>(&Ws[r * P + col]) = *reinterpret_cast<const uint4*>(src + 8 * x);
     }
   }
-  __syncthreads();
-  const size_t rs = (size_t)H * D;
-  const int ntile = (tok_end - tok_begin + 127) / 128;
+  const size_t rs = (size_t)H * D;                 // token stride (elements)
+  const int ntile = (tok_end - tok_begin + Cfg::TT - 1) / Cfg::TT;
+  const int tr = 32 * (w & 1);                     // this wave's first token row in the tile
+  const int ab0 = NAB * (w >> 1);                  // this wave's first 32-row output block
+  // direct-load lane pattern: row L / RPL of the 1 KiB block, logical chunk (L % RPL) ^ swz
+  const int lrow = lane / RPL, lpos = lane % RPL;
+
   for (int tile = blockIdx.x; tile < ntile; tile += gridDim.x) {
-    // keep W's fragments in LDS: re-read them per tile instead of pinning
-    // D*D/32 registers per lane for the whole loop
-    asm volatile("" ::: "memory");
-    const int tok = tok_begin + tile * 128 + 32 * w + j;
-    const bool valid = tok < tok_end;
-    const size_t off = (size_t)tok * rs + (size_t)h * D;
-    bf16x8 qb[D / 16];
+    const int t0 = tok_begin + tile * Cfg::TT;
+    // ---- q and O rows of the tile -> LDS (rows past the chunk repeat its last row);
+    // the buffer base (wave-uniform) is the tile's first row, lanes add row offsets
+    const size_t base = ((size_t)t0 * rs + (size_t)h * D) * 2;
+    const uint32_t span = (uint32_t)(Cfg::TT * rs * 2);
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(reinterpret_cast<const unsigned char*>(q) + base, span);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(reinterpret_cast<const unsigned char*>(O) + base, span);
+    for (int i = w; i < Cfg::LOADS; i += 4) {
+      const int r = RPI * i + lrow;
+      const int tok = min(t0 + r, tok_end - 1);
+      const uint32_t off = (uint32_t)((tok - t0) * rs * 2) + 16u * (lpos ^ swz_rows(r, RB));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void_ptr)(qt + 1024 * i), 16, off, 0, 0, 0);
+      if (ACC) __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_void_ptr)(ot + 1024 * i), 16, off, 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();     // tile (and, on the first pass, W) in LDS
+
+    // ---- O_lin^T for this wave's 32 tokens x 32*NAB output rows (d = 32: two waves)
+    if ((w >> 1) < Cfg::NWR) {
+    floatx16 acc[NAB];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      qb[s] = valid ? *reinterpret_cast<const bf16x8*>(q + off + 16 * s + 8 * hf) : bf16x8{};
+    for (int x = 0; x < NAB; ++x) acc[x] = floatx16{};
+    const int r = tr + j;
 #pragma unroll
-    for (int ab = 0; ab < NDB; ++ab) {
-      floatx16 acc = floatx16{};
+    for (int s = 0; s < D / 16; ++s) {
+      const bf16x8 qb = *reinterpret_cast<const bf16x8*>(qt + r * RB + 16 * ((2 * s + hf) ^ swz_rows(r, RB)));
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const bf16x8 whi = *reinterpret_cast<const bf16x8*>(&Ws[0][(32 * ab + j) * P + 16 * s + 8 * hf]);
-        const bf16x8 wlo = *reinterpret_cast<const bf16x8*>(&Ws[1][(32 * ab + j) * P + 16 * s + 8 * hf]);
-        acc = mfma_bf16(whi, qb[s], acc);
-        acc = mfma_bf16(wlo, qb[s], acc);
-      }
-      if (valid) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint16_t* dst = O + off + 32 * ab + 8 * g + 4 * hf;
-          float x0 = acc[4 * g], x1 = acc[4 * g + 1], x2 = acc[4 * g + 2], x3 = acc[4 * g + 3];
-          if (ACC) {
-            const uint2 old = *reinterpret_cast<const uint2*>(dst);
-            x0 += __uint_as_float(old.x << 16);
-            x1 += __uint_as_float(old.x & 0xffff0000u);
-            x2 += __uint_as_float(old.y << 16);
-            x3 += __uint_as_float(old.y & 0xffff0000u);
-          }
-          *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
-        }
+      for (int x = 0; x < NAB; ++x) {
+        const bf16x8 wa = *reinterpret_cast<const bf16x8*>(&Ws[(32 * (ab0 + x) + j) * P + 16 * s + 8 * hf]);
+        acc[x] = mfma_bf16(wa, qb, acc[x]);
       }
     }
+    // ---- O tile in LDS <- O (+) O_lin: accumulator element 4g + i of block ab is
+    // output row 32*ab + 8g + 4*hf + i, i.e. bytes 8*hf.. of chunk 4*ab + g
+#pragma unroll
+    for (int x = 0; x < NAB; ++x)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        unsigned char* cell = ot + r * RB + 16 * ((4 * (ab0 + x) + g) ^ swz_rows(r, RB)) + 8 * hf;
+        float x0 = acc[x][4 * g], x1 = acc[x][4 * g + 1], x2 = acc[x][4 * g + 2], x3 = acc[x][4 * g + 3];
+        if (ACC) {
+          const uint2 old = *reinterpret_cast<const uint2*>(cell);
+          x0 += __uint_as_float(old.x << 16);
+          x1 += __uint_as_float(old.x & 0xffff0000u);
+          x2 += __uint_as_float(old.y << 16);
+          x3 += __uint_as_float(old.y & 0xffff0000u);
+        }
+        *reinterpret_cast<uint2*>(cell) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
+      }
+    }
+    __syncthreads();     // O tile complete
+
+    // ---- O tile -> global, whole rows
+    for (int i = w; i < Cfg::LOADS; i += 4) {
+      const int rr = RPI * i + lrow;
+      const int tok = t0 + rr;
+      if (tok < tok_end) {
+        const uint4 vv = *reinterpret_cast<const uint4*>(ot + 1024 * i + 16 * lane);   // row rr, position lpos
+        const int chunk = lpos ^ swz_rows(rr, RB);
+        *reinterpret_cast<uint4*>(O + (size_t)tok * rs + (size_t)h * D + 8 * chunk) = vv;
+      }
+    }
+    __syncthreads();     // tile buffers free for the next tile
   }
 }
 
@@ -535,7 +581,7 @@ hipError_t launch_readout(int prec, const void* q, const void* W, int F, int N, 
     return hipGetLastError();
   }
   const int max_tiles = (kChunk * N + 127) / 128;
-  const int rx = max_tiles < 8 ? max_tiles : 8;
+  const int rx = max_tiles < 16 ? max_tiles : 16;
   const dim3 grid(rx, C, H);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* ww = static_cast<const uint16_t*>(W);
