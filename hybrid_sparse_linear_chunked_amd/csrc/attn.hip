@@ -41,6 +41,14 @@ __device__ inline int vt_pos_of_key(int n) {   // n in [0, 64)
 // grid (F, H), 512 threads.  LDS: K^T and V^T of one 64-token tile, keys permuted
 // as in the vt layout (the Gram products only need both operands in the same
 // token order).
+//
+// The transpose happens in registers: a thread loads four token rows x 8
+// channels (four 16-byte pieces, coalesced across the wave), regroups them into
+// 8 channels x four tokens with 16-bit permutes, and writes 8-byte pieces to
+// LDS.  The four tokens are the ones the vt permutation puts at consecutive
+// positions, so the pieces land as whole runs of a V^T row.  The next tile's
+// loads are in flight while this tile's V^T block is written out and its Gram
+// MFMAs run.
 template <int D>
 __global__ __launch_bounds__(512) void prep_kernel(const uint16_t* __restrict__ k,
                                                    const uint16_t* __restrict__ v, int F, int N,
@@ -51,6 +59,8 @@ __global__ __launch_bounds__(512) void prep_kernel(const uint16_t* __restrict__ 
   constexpr int NB = D / 32;                     // 32-channel blocks per side
   constexpr int NBLK = 2 * NB * NB;              // G blocks then B blocks
   constexpr int PER_WAVE = (NBLK + 7) / 8;
+  constexpr int ACTIVE = 4 * D;                  // loading threads: 2 tensors x 8 key pieces x D/8 groups x 2 halves
+  static_assert(ACTIVE <= 512, "one 4-token x 8-channel piece per loading thread");
   __shared__ __attribute__((aligned(16))) uint16_t KT[D * P];
   __shared__ __attribute__((aligned(16))) uint16_t VT[D * P];
 
@@ -61,32 +71,50 @@ __global__ __launch_bounds__(512) void prep_kernel(const uint16_t* __restrict__ 
   const bool grams = do_grams && f > 0 && f < F - 1;
   const size_t rs = (size_t)H * D;               // token stride (elements)
 
+  // this thread's piece: tensor, 8-position run pc of the permuted key order,
+  // channel group cg, half th of the run (positions 8*pc + 4*th .. +4)
+  const bool loader = tid < ACTIVE;
+  const int isv = tid / (2 * D), rem = tid % (2 * D);
+  const int pc = rem & 7, cg = (rem >> 3) % (D / 8), th = rem / D;
+  const uint16_t* src = (isv ? v : k) + (size_t)f * N * rs + (size_t)h * D + 8 * cg;
+  // key of position 8*pc + 4*th + e (inverse of vt_pos_of_key)
+  const int key0 = 16 * (pc >> 1) + 4 * (pc & 1) + 8 * th;
+  uint4 raw[4];
+  auto load = [&](int b) {
+    const int nvalid = min(64, N - 64 * b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int n = key0 + e;
+      raw[e] = (loader && n < nvalid) ? *reinterpret_cast<const uint4*>(src + (size_t)(64 * b + n) * rs)
+                                      : make_uint4(0, 0, 0, 0);
+    }
+  };
+
   floatx16 acc[PER_WAVE];
 #pragma unroll
   for (int x = 0; x < PER_WAVE; ++x) acc[x] = floatx16{};
 
+  load(0);
   for (int b = 0; b < nb; ++b) {
-    const int nvalid = min(64, N - 64 * b);
-    // global -> registers -> LDS (transposed, permuted keys)
-    constexpr int CH = 64 * D / 8;               // 16-byte chunks per tensor tile
-    for (int c = tid; c < 2 * CH; c += 512) {
-      const bool isv = c >= CH;
-      const int cc = isv ? c - CH : c;
-      const int n = cc / (D / 8), c8 = cc % (D / 8);
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (n < nvalid) {
-        const uint16_t* src = (isv ? v : k) + ((size_t)f * N + 64 * b + n) * rs + (size_t)h * D + 8 * c8;
-        val = *reinterpret_cast<const uint4*>(src);
-      }
+    // ---- 4 tokens x 8 channels -> 8 channels x 4 tokens -> LDS
+    if (loader) {
       uint16_t* T = isv ? VT : KT;
-      const int p = vt_pos_of_key(n);
-      const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
+      const uint32_t r0[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
+      const uint32_t r1[4] = {raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+      const uint32_t r2[4] = {raw[2].x, raw[2].y, raw[2].z, raw[2].w};
+      const uint32_t r3[4] = {raw[3].x, raw[3].y, raw[3].z, raw[3].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        T[(8 * c8 + e) * P + p] = static_cast<uint16_t>(wv[e >> 1] >> (16 * (e & 1)));
+      for (int m = 0; m < 4; ++m) {
+        // channels 2m (low halves) and 2m+1 (high halves) of the four tokens
+        const uint2 lo = make_uint2((r0[m] & 0xffffu) | (r1[m] << 16), (r2[m] & 0xffffu) | (r3[m] << 16));
+        const uint2 hi = make_uint2((r0[m] >> 16) | (r1[m] & 0xffff0000u), (r2[m] >> 16) | (r3[m] & 0xffff0000u));
+        *reinterpret_cast<uint2*>(&T[(8 * cg + 2 * m) * P + 8 * pc + 4 * th]) = lo;
+        *reinterpret_cast<uint2*>(&T[(8 * cg + 2 * m + 1) * P + 8 * pc + 4 * th]) = hi;
+      }
     }
     __syncthreads();
-    // V^T block out: D rows x 64 keys
+    if (b + 1 < nb) load(b + 1);
+    // ---- V^T block out: D rows x 64 keys
     {
       uint16_t* dst = vt + (((size_t)h * F + f) * nb + b) * (size_t)(D * 64);
       for (int c = tid; c < D * 8; c += 512) {
