@@ -71,30 +71,33 @@ __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__
 }
 
 // ============================================================ per-frame affine maps
-// grid (F-2, H), 256 threads; frame t = blockIdx.x + 1.
+// grid (F-2, H), 1024 threads (16 waves, 4 per SIMD to hide the latency of the
+// serial column steps); frame t = blockIdx.x + 1.
 // In:  G = K K^T, B = V K^T of frame t.   Out (in place): G <- M = A^-1,
 // B <- C = beta B M, with A = I + beta G.
 //   1. Cholesky A = L L^T, right-looking: the matrix lives in registers (thread
-//      (ty, tx) of a 16 x 16 grid owns an RB x RB block), the pivot column is
+//      (ty, tx) of a 32 x 32 grid owns an RB x RB block), the pivot column is
 //      broadcast through LDS, one barrier per column.
 //   2. Y = L^-1 by forward substitution on the identity, same layout, pivot row
 //      broadcast through LDS.
 //   3. M = Y^T Y and C = beta B M with fp32 MFMA (32x32x2) from LDS.
 template <int D>
-__global__ __launch_bounds__(256) void factor_kernel(float* __restrict__ G, float* __restrict__ Bm,
-                                                     const float* __restrict__ beta, int F, int H) {
-  constexpr int RB = D / 16;
+__global__ __launch_bounds__(1024) void factor_kernel(float* __restrict__ G, float* __restrict__ Bm,
+                                                      const float* __restrict__ beta, int F, int H) {
+  constexpr int TG = 32;          // thread grid side
+  constexpr int NT = TG * TG;
+  constexpr int RB = D / TG;
   constexpr int LP = D + 1;
   constexpr int NB = D / 32;
   constexpr int NBLK = NB * NB;
-  constexpr int PER_WAVE = (NBLK + 3) / 4;
+  constexpr int PER_WAVE = (NBLK + NT / 64 - 1) / (NT / 64);
   extern __shared__ float sm[];
   float* Ls = sm;                 // [D][LP]: L, later M
   float* Xs = sm + D * LP;        // [D][LP]: Y, later B
   float* cbuf = Xs + D * LP;      // [2][D]
 
   const int t = blockIdx.x + 1, h = blockIdx.y;
-  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int tid = threadIdx.x, ty = tid / TG, tx = tid % TG;
   const int lane = tid & 63, w = tid >> 6, j = lane & 31, hf = lane >> 5;
   const float b = beta[(size_t)t * H + h];
   float* Gp = G + ((size_t)t * H + h) * D * D;
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(256) void factor_kernel(float* __restrict__ G, floa
     }
 
   // ---- 1. Cholesky
-  for (int jb = 0; jb < 16; ++jb) {
+  for (int jb = 0; jb < TG; ++jb) {
 #pragma unroll
     for (int jr = 0; jr < RB; ++jr) {
       const int jj = jb * RB + jr;
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(256) void factor_kernel(float* __restrict__ G, floa
   for (int ii = 0; ii < RB; ++ii)
 #pragma unroll
     for (int kk = 0; kk < RB; ++kk) a[ii][kk] = (ty * RB + ii == tx * RB + kk) ? 1.f : 0.f;
-  for (int kb = 0; kb < 16; ++kb) {
+  for (int kb = 0; kb < TG; ++kb) {
 #pragma unroll
     for (int kr = 0; kr < RB; ++kr) {
       const int k = kb * RB + kr;
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(256) void factor_kernel(float* __restrict__ G, floa
       }
     }
   }
-  for (int e = tid; e < D * D; e += 256) Xs[(e / D) * LP + (e % D)] = Bp[e];
+  for (int e = tid; e < D * D; e += NT) Xs[(e / D) * LP + (e % D)] = Bp[e];
   __syncthreads();
 
   // ---- 3b. C = beta B M  (C[a][b] = beta sum_k B[a][k] M[k][b])
@@ -532,7 +535,7 @@ static hipError_t factor_d(float* G, float* B, const float* beta, int F, int H, 
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(factor_kernel<D>, dim3(F - 2, H), dim3(256), lds, st, G, B, beta, F, H);
+  hipLaunchKernelGGL(factor_kernel<D>, dim3(F - 2, H), dim3(1024), lds, st, G, B, beta, F, H);
   return hipGetLastError();
 }
 
