@@ -65,7 +65,7 @@ def algorithmic_work(F, N, H, d):
                 readout_bytes=ro_bytes)
 
 
-PROFILE = {3: os.path.join(ROOT, "profiles", "attn_lds_kernel_768p_14s.txt")}
+PROFILE = {3: os.path.join(ROOT, "profiles", "layer_kernels_768p_14s.txt")}
 
 
 def measured_traffic(config):
@@ -88,25 +88,29 @@ def measured_traffic(config):
     return traffic if recorded == sha else None
 
 
-def cpu_baseline(F, N, H, d, seed=0, tokens=384):
+def cpu_baseline(F, N, H, d, seed=0, tokens=1024):
     """Time the fp64 oracle on a bounded sample of the workload and extrapolate to
-    one layer (ms).  Sample: head 0; the softmax of `tokens` query tokens of one
-    query frame of every work class (anchor / edge chunk / next-to-edge / interior);
-    head 0's whole forward + backward state computation; one frame's readout."""
+    one layer (ms).  Sample: heads 0 and H-1; the softmax of `tokens` query tokens
+    of one query frame of every work class (anchor / edge chunk / next-to-edge /
+    interior); both heads' whole forward + backward state computation; one frame's
+    readout per head."""
     import numpy as np
     import torch
     import threadpoolctl
     import vdn_synth
     from oracle import vdn_oracle as orc
 
+    heads = sorted({0, H - 1})
+
     def gen(name):
-        out = torch.empty((F, N, 1, d), dtype=torch.bfloat16)
-        vdn_synth.tensor(name, F, N, H, d, seed=seed, heads=[0], out=out,
+        out = torch.empty((F, N, len(heads), d), dtype=torch.bfloat16)
+        vdn_synth.tensor(name, F, N, H, d, seed=seed, heads=heads, out=out,
                          convert=lambda b: torch.from_numpy(b).to(torch.bfloat16))
         return out.to(torch.float64).numpy()
 
     q, k, v = gen("q"), gen("k"), gen("v")
-    beta = vdn_synth.beta(F, H, seed=seed).astype(np.float64)[:, :1]
+    beta = vdn_synth.beta(F, H, seed=seed).astype(np.float64)[:, heads]
+    hs = list(range(len(heads)))
     classes = {}
     for i in range(F):
         classes.setdefault(len(orc.softmax_frames(i, F)), []).append(i)
@@ -115,27 +119,29 @@ def cpu_baseline(F, N, H, d, seed=0, tokens=384):
     for nk, frames in sorted(classes.items()):
         i = frames[len(frames) // 2]
         a = time.perf_counter()
-        orc.softmax_branch(q, k, v, frames=[i], heads=[0], tokens=range(tokens))
+        orc.softmax_branch(q, k, v, frames=[i], heads=hs, tokens=range(tokens))
         per_token = (time.perf_counter() - a) / tokens
         soft_s += per_token * N * len(frames)
     a = time.perf_counter()
     Sf, Sb = orc.vda_states(k, v, beta)
     states_s = time.perf_counter() - a
     a = time.perf_counter()
-    mid = F // 2
-    orc.linear_branch(q, Sf, Sb, frames=[mid])
+    orc.linear_branch(q, Sf, Sb, frames=[F // 2])
     readout_s = (time.perf_counter() - a) * max(F - 2, 0)
     sample_s = time.perf_counter() - t0
-    layer_ms = 1000.0 * H * (soft_s + states_s + readout_s)
+    per_head = (soft_s + states_s + readout_s) / len(heads)
+    layer_ms = 1000.0 * H * per_head
     info = threadpoolctl.threadpool_info()
     cores = max([x.get("num_threads", 1) for x in info] or [1])
+    blas = ",".join(sorted({f"{x.get('internal_api')} {x.get('version')}" for x in info if x.get("user_api") == "blas"}))
     return {
         "value": layer_ms, "unit": "ms", "cores": cores, "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle, head 0 of {H}: softmax of {tokens} query tokens of one frame "
+        "sample": (f"fp64 NumPy oracle, heads {heads} of {H}: softmax of {tokens} query tokens of one frame "
                    f"per work class ({len(classes)} classes), full forward+backward VDA states, one "
-                   f"frame's readout; extrapolated by token/frame counts and x{H} heads; "
+                   f"frame's readout; extrapolated by token/frame counts and to {H} heads; "
                    f"{sample_s:.1f} s of CPU work"),
-        "sample_seconds": sample_s,
+        "sample_seconds": round(sample_s, 2),
+        "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count(), "blas": blas,
     }
 
 
