@@ -899,7 +899,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
     float mx = __builtin_fmaxf(s[0][0], s[1][0]);
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[0][e]), s[1][e]);
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair_max(mx);
     const float mt = mx * scale;
     if (__any(mt > m_run + kLazy)) {
       const float m_new = __builtin_fmaxf(m_run, mt);
@@ -949,7 +949,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   }
 
   // ---- epilogue
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   if (!qvalid) return;
   if (it.split < 0) {
     const float inv = 1.f / l_tot;

@@ -86,6 +86,17 @@ __device__ inline floatx16 mfma_fp8(const intx8& a, const intx8& b, const floatx
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// max / sum of x over the lane pair (j, j + 32), in both lanes: v_permlane32_swap
+// exchanges the two halves of the wave on the VALU, without an LDS round trip
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ inline float wave_max(float x) {
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
   return x;
