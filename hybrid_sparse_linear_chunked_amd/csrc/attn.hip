@@ -752,6 +752,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   }
   float scale = a.scale_log2;
   if constexpr (FP8) scale *= (a.amax[h] * (1.f / 448.f)) * (a.amax[H + h] * (1.f / 448.f));
+  if constexpr (!FP8) {
+    // bf16: the Q operand carries the factor log2(e)/sqrt(d) (rounded once to
+    // bf16), so the MFMAs deliver scores in log2 units directly
+#pragma unroll
+    for (int s = 0; s < Cfg::QSTEPS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[s][e] = (__bf16)((float)qb[s][e] * scale);
+  }
 
   // ---- global -> LDS tile loads
   const unsigned char* kbase = FP8 ? reinterpret_cast<const unsigned char*>(a.k8)
@@ -830,7 +838,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   floatx16 o[NDB];
 #pragma unroll
   for (int x = 0; x < NDB; ++x) o[x] = floatx16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // running max m (log2 units).  bf16: the Q.K^T accumulators start at -m, so
+  // the MFMAs leave s - m and the exponent needs no VALU op; m is finite from the
+  // start and the first tile sets it to that tile's maximum
+  float m_run = FP8 ? -INFINITY : 0.f, l_run = 0.f;
 
 #pragma unroll
   for (int x = 0; x < AHEAD; ++x) {
@@ -859,7 +870,17 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
     constexpr int NQK = 2 * Cfg::QSTEPS, QB = NQK < kQkBatch ? NQK : kQkBatch, NQB = NQK / QB;
     typename LdsCfg<D, PREC>::KFrag kf[2][QB];
     bf16x8 va[2][NDB];
-    floatx16 s[2] = {floatx16{}, floatx16{}};
+    floatx16 s[2];
+    if constexpr (FP8) {
+      s[0] = floatx16{};
+      s[1] = floatx16{};
+    } else {
+      floatx16 nm;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) nm[r] = -m_run;
+      s[0] = nm;
+      s[1] = nm;
+    }
 #pragma unroll
     for (int x = 0; x < QB; ++x) kf[0][x] = Cfg::kfrag(sbase, x, j, hf);
 #pragma unroll
@@ -900,16 +921,39 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[0][e]), s[1][e]);
     mx = pair_max(mx);
-    const float mt = mx * scale;
-    if (__any(mt > m_run + kLazy)) {
-      const float m_new = __builtin_fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+    if constexpr (FP8) {
+      const float mt = mx * scale;
+      if (__any(mt > m_run + kLazy)) {
+        const float m_new = __builtin_fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int x = 0; x < NDB; ++x) o[x] *= alpha;
+        for (int x = 0; x < NDB; ++x) o[x] *= alpha;
+      }
+    } else {
+      // scores are s - m already: raise m by the excess (on the first tile, by the
+      // tile maximum whatever its sign; nothing is accumulated yet to rescale)
+      if (t == 0 || __any(mx > kLazy)) {
+        const float dm = t == 0 ? mx : __builtin_fmaxf(mx, 0.f);
+        if (t != 0) {
+          const float alpha = __builtin_amdgcn_exp2f(-dm);
+          l_run *= alpha;
+#pragma unroll
+          for (int x = 0; x < NDB; ++x) o[x] *= alpha;
+        }
+        m_run += dm;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] -= dm;
+      }
     }
     const float neg_m = -m_run;
+    // exponent of a score: bf16 scores are already s - m in log2 units
+    auto expo = [&](float x) {
+      return FP8 ? __builtin_amdgcn_exp2f(fmaf(x, scale, neg_m)) : __builtin_amdgcn_exp2f(x);
+    };
 
     // ---- O^T += V^T P^T, one group of 16 keys per batch; the probabilities of
     // the next group are formed on the VALU while this group's MFMAs run, and
@@ -918,7 +962,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
     float psum = 0.f;
     bf16x8 pb[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pb[0][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[0][e], scale, neg_m));
+    for (int e = 0; e < 8; ++e) pb[0][e] = (__bf16)expo(s[0][e]);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (VDN_LDS_WAITALL) lds_wait_all();
@@ -933,7 +977,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
         const int kb = (u + 1) >> 1, e0 = 8 * ((u + 1) & 1);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          pb[(u + 1) & 1][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][e0 + e], scale, neg_m));
+          pb[(u + 1) & 1][e] = (__bf16)expo(s[kb][e0 + e]);
       }
 #pragma unroll
       for (int e = 0; e < 8; e += 2)
