@@ -842,6 +842,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   // the MFMAs leave s - m and the exponent needs no VALU op; m is finite from the
   // start and the first tile sets it to that tile's maximum
   float m_run = FP8 ? -INFINITY : 0.f, l_run = 0.f;
+  floatx16 nm = floatx16{};      // -m in every element: the first Q.K^T accumulator input
 
 #pragma unroll
   for (int x = 0; x < AHEAD; ++x) {
@@ -875,9 +876,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       s[0] = floatx16{};
       s[1] = floatx16{};
     } else {
-      floatx16 nm;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) nm[r] = -m_run;
       s[0] = nm;
       s[1] = nm;
     }
@@ -947,7 +945,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[kb][r] -= dm;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) nm[r] = -m_run;
       }
+      asm volatile("" : "+v"(nm));   // keep it in registers rather than rebuild it every tile
     }
     const float neg_m = -m_run;
     // exponent of a score: bf16 scores are already s - m in log2 units
