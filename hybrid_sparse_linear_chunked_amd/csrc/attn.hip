@@ -635,7 +635,6 @@ __device__ inline void lds_wait_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 template <int KX, int VX>
 struct LaneOffsets {
   uint32_t koff[KX], voff[VX];
-  int krow[KX], kchk[KX];
 };
 
 struct Item {
@@ -778,14 +777,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   LaneOffsets<KX, VX> lo;
   uint32_t* koff = lo.koff;
   uint32_t* voff = lo.voff;
-  int* krow = lo.krow;
-  int* kchk = lo.kchk;
 #pragma unroll
   for (int x = 0; x < KX; ++x) {
     const int ii = w * KX + x;
-    krow[x] = ii * Cfg::K_RPI + lane / Cfg::KCH;
-    kchk[x] = (lane % Cfg::KCH) ^ Cfg::swz_k(krow[x]);
-    koff[x] = (uint32_t)(krow[x] * krs) + 16u * kchk[x];
+    const int krow = ii * Cfg::K_RPI + lane / Cfg::KCH;
+    koff[x] = (uint32_t)(krow * krs) + 16u * ((lane % Cfg::KCH) ^ Cfg::swz_k(krow));
   }
 #pragma unroll
   for (int x = 0; x < VX; ++x) {
@@ -801,15 +797,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
     // buffer loads to LDS (MUBUF): unlike the FLAT-encoded global_load_lds they
     // leave the compiler free to wait for LDS reads one by one (lgkmcnt(n))
     const unsigned char* kt = kbase + (((size_t)f * N + BK * b) * rs + (size_t)h * D) * (FP8 ? 1 : 2);
-    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kt, (uint32_t)(BK * krs));
+    // the resource ends with the frame: rows past its end read as zeros (their
+    // scores are masked)
+    const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kt, (uint32_t)(nvalid * krs));
 #pragma unroll
     for (int x = 0; x < KX; ++x) {
       if (x < x0 || x >= x1) continue;
       if (Cfg::K_INSTR % NW != 0 && w * KX + x >= Cfg::K_INSTR) break;
-      // rows past the frame's end re-read its last row (their scores are masked)
-      const uint32_t off = nvalid == BK ? koff[x]
-                                        : (uint32_t)(min(krow[x], nvalid - 1) * krs) + 16u * kchk[x];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_ptr)(sbase + 1024 * (w * KX + x)), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_ptr)(sbase + 1024 * (w * KX + x)), 16, koff[x], 0, 0, 0);
     }
     const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(
         a.vt + (((size_t)h * F + f) * nb + b) * (size_t)(D * BK));
