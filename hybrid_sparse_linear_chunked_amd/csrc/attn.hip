@@ -586,46 +586,43 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 // Same work items and arithmetic as attn_kernel, with K and V^T tiles moved
 // global -> LDS by the 16-byte direct loads of gfx950 (buffer_load_dwordx4 ...
 // lds): no staging registers, no LDS store instructions.  A direct load writes
-// the 64 lanes' 16-byte pieces to 1 KiB of consecutive LDS, so bank conflicts
-// are avoided with an XOR swizzle of the 16-byte chunks inside a row instead of
-// row padding: chunk c of row r sits at position c ^ swz(r).
+// the 64 lanes' 16-byte pieces to 1 KiB of consecutive LDS; every LDS row holds
+// one 16-byte padding chunk after its data (the lane that lands there re-reads a
+// chunk of the row), so 16 consecutive rows read at one chunk hit 16 distinct
+// bank groups, and the address of every operand fragment is one lane register
+// plus an immediate offset.
 template <int D, int PREC>
 struct LdsCfg {
   static constexpr bool FP8 = PREC == 2;
-  static constexpr int KROW = FP8 ? D : 2 * D;     // bytes per K row
+  static constexpr int KROW = FP8 ? D : 2 * D;     // bytes per K row in global memory
   static constexpr int KCH = KROW / 16;            // 16-byte chunks per K row
-  static constexpr int K_BYTES = BK * KROW;
-  static constexpr int V_BYTES = D * BK * 2;       // V^T: D rows x 64 keys bf16 (128 B)
+  static constexpr int KP = 16 * (KCH + 1);        // LDS pitch of a K row
+  static constexpr int VP = 16 * 9;                // LDS pitch of a V^T row (64 keys bf16 + pad)
+  static constexpr int K_INSTR = KCH + 1;          // wave-wide direct loads per K tile (64 rows)
+  static constexpr int V_INSTR = (9 * D + 63) / 64;
+  static constexpr int K_BYTES = 1024 * K_INSTR;
+  static constexpr int V_BYTES = 1024 * V_INSTR;
   static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int K_INSTR = K_BYTES / 1024;   // wave-wide direct loads per K tile
-  static constexpr int V_INSTR = V_BYTES / 1024;
-  static constexpr int K_RPI = 1024 / KROW;        // K rows per direct load
   static constexpr int QSTEPS = FP8 ? D / 64 : D / 16;
-  static_assert(K_INSTR >= 1 && V_INSTR >= 1, "a tile is at least one wave-wide load");
-  // chunk c of row r sits at position c ^ swz(r) (swz_rows in common.h)
-  __device__ static int swz_k(int r) { return swz_rows(r, KROW); }
-  __device__ static int swz_v(int r) { return swz_rows(r, 128); }
+  static_assert(BK * (KCH + 1) == 64 * K_INSTR, "a K tile is whole wave-wide loads");
   // LDS operand of one Q.K^T MFMA: K rows 32*kb + (lane & 31), reduction step
   // st, for item i = 2*st + kb (bf16: 16 dims; fp8: 64 dims)
   using KFrag = typename std::conditional<FP8, intx8, bf16x8>::type;
   __device__ static KFrag kfrag(const unsigned char* sbase, int i, int j, int hf) {
     const int st = i >> 1, kb = i & 1;
-    const int r = 32 * kb + j;
-    const unsigned char* krow = sbase + r * KROW;
-    const int sw = swz_k(r);
+    const unsigned char* krow = sbase + (32 * kb + j) * KP;
     if constexpr (FP8) {
       const int c0 = 4 * st + 2 * hf;
-      const uint4 x0 = *reinterpret_cast<const uint4*>(krow + 16 * (c0 ^ sw));
-      const uint4 x1 = *reinterpret_cast<const uint4*>(krow + 16 * ((c0 + 1) ^ sw));
+      const uint4 x0 = *reinterpret_cast<const uint4*>(krow + 16 * c0);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(krow + 16 * (c0 + 1));
       return KFrag{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     } else {
-      return *reinterpret_cast<const bf16x8*>(krow + 16 * ((2 * st + hf) ^ sw));
+      return *reinterpret_cast<const bf16x8*>(krow + 16 * (2 * st + hf));
     }
   }
   // LDS operand of one P.V MFMA: V^T rows 32*db + (lane & 31), keys 16u..16u+15
   __device__ static bf16x8 vfrag(const unsigned char* vbase, int u, int db, int j, int hf) {
-    const int r = 32 * db + j;
-    return *reinterpret_cast<const bf16x8*>(vbase + r * 128 + 16 * ((2 * u + hf) ^ swz_v(r)));
+    return *reinterpret_cast<const bf16x8*>(vbase + (32 * db + j) * VP + 16 * (2 * u + hf));
   }
 };
 
@@ -770,8 +767,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   // the token-major k tensor) and a V^T block; the tile base is wave-uniform.
   // (Kept in a struct: clang drops the host launch stub of a kernel template
   // whose lambda captures local arrays sized by a dependent constant.)
-  // every wave issues KX of the tile's K loads and VX of its V loads (the last
-  // waves fewer when the count does not divide)
+  // load ii of a tile is issued by wave ii % NW as its load ii / NW; lane L of
+  // load ii fills LDS chunk q = 64 ii + L, i.e. row q / pitch, chunk q % pitch
+  // (the padding chunk re-reads the row's last chunk; rows past a V^T block's
+  // end, in its last partial load, re-read its last row)
   constexpr int KX = (Cfg::K_INSTR + NW - 1) / NW, VX = (Cfg::V_INSTR + NW - 1) / NW;
   const size_t krs = rs * (FP8 ? 1 : 2);             // token stride in bytes
   LaneOffsets<KX, VX> lo;
@@ -779,15 +778,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   uint32_t* voff = lo.voff;
 #pragma unroll
   for (int x = 0; x < KX; ++x) {
-    const int ii = w * KX + x;
-    const int krow = ii * Cfg::K_RPI + lane / Cfg::KCH;
-    koff[x] = (uint32_t)(krow * krs) + 16u * ((lane % Cfg::KCH) ^ Cfg::swz_k(krow));
+    const int q = 64 * (x * NW + w) + lane;
+    const int row = q / (Cfg::KCH + 1), c = min(q % (Cfg::KCH + 1), Cfg::KCH - 1);
+    koff[x] = (uint32_t)(row * krs) + 16u * c;
   }
 #pragma unroll
   for (int x = 0; x < VX; ++x) {
-    const int ii = w * VX + x;
-    const int r = ii * 8 + (lane >> 3);
-    voff[x] = (uint32_t)(r * 128 + 16 * ((lane & 7) ^ Cfg::swz_v(r)));
+    const int q = 64 * (x * NW + w) + lane;
+    const int row = min(q / 9, D - 1), c = min(q % 9, 7);
+    voff[x] = (uint32_t)(row * 128 + 16 * c);
   }
   // loads [x0, x1) of this wave's share of a tile: K loads first, then V^T loads
   constexpr int LPT = KX + VX;
@@ -803,8 +802,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
 #pragma unroll
     for (int x = 0; x < KX; ++x) {
       if (x < x0 || x >= x1) continue;
-      if (Cfg::K_INSTR % NW != 0 && w * KX + x >= Cfg::K_INSTR) break;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_ptr)(sbase + 1024 * (w * KX + x)), 16, koff[x], 0, 0, 0);
+      if (x * NW + w >= Cfg::K_INSTR) break;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_ptr)(sbase + 1024 * (x * NW + w)), 16, koff[x], 0, 0, 0);
     }
     const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(
         a.vt + (((size_t)h * F + f) * nb + b) * (size_t)(D * BK));
@@ -812,8 +811,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
 #pragma unroll
     for (int x = 0; x < VX; ++x) {
       if (KX + x < x0 || KX + x >= x1) continue;
-      if (Cfg::V_INSTR % NW != 0 && w * VX + x >= Cfg::V_INSTR) break;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void_ptr)(sbase + Cfg::K_BYTES + 1024 * (w * VX + x)), 16,
+      if (x * NW + w >= Cfg::V_INSTR) break;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void_ptr)(sbase + Cfg::K_BYTES + 1024 * (x * NW + w)), 16,
                                                voff[x], 0, 0, 0);
     }
   };
