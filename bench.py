@@ -88,7 +88,7 @@ def measured_traffic(config):
     return traffic if recorded == sha else None
 
 
-def cpu_baseline(F, N, H, d, seed=0, tokens=2048):
+def cpu_baseline(F, N, H, d, seed=0, tokens=2560):
     """Time the fp64 oracle on a bounded sample of the workload and extrapolate to
     one layer (ms).  Sample: heads 0 and H-1; the softmax of `tokens` query tokens
     of one query frame of every work class (anchor / edge chunk / next-to-edge /
