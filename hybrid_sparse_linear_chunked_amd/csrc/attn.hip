@@ -720,6 +720,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   const int nb = (N + BK - 1) / BK;
   // the item is wave-uniform; say so, so that tile bookkeeping stays in SGPRs
   const Item it = uniform_item(decode_item(a));
+  // the second wave of every SIMD issues first when both are ready: a fixed order
+  // for the two waves that share the matrix core (measured 0.5-1 % faster than
+  // the hardware's default arbitration; the reverse order gains the same)
+  if (w >= NW / 2) __builtin_amdgcn_s_setprio(1);
   const int h = it.h;
   const int ntiles = it.nslots * nb;
 
