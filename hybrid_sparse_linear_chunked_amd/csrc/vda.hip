@@ -71,19 +71,25 @@ __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__
 }
 
 // ============================================================ per-frame affine maps
-// grid (F-2, H), 1024 threads (16 waves, 4 per SIMD to hide the latency of the
-// serial column steps); frame t = blockIdx.x + 1.
+// grid (F-2, H), 1024 threads (16 waves; two workgroups per CU, so 8 waves per
+// SIMD hide the latency of the serial column steps); frame t = blockIdx.x + 1.
 // In:  G = K K^T, B = V K^T of frame t.   Out (in place): G <- M = A^-1,
 // B <- C = beta B M, with A = I + beta G.
-//   1. Cholesky A = L L^T, right-looking: the matrix lives in registers (thread
-//      (ty, tx) of a 32 x 32 grid owns an RB x RB block), the pivot column is
-//      broadcast through LDS, one barrier per column.
-//   2. Y = L^-1 by forward substitution on the identity, same layout, pivot row
-//      broadcast through LDS.
-//   3. M = Y^T Y and C = beta B M with fp32 MFMA (32x32x2) from LDS.
+//   1. Cholesky A = L L^T, right-looking, and in the same column steps Y = L^-1
+//      by right-looking forward substitution on the identity: both matrices live
+//      in registers (thread (ty, tx) of a 32 x 32 grid owns an RB x RB block of
+//      each); step j broadcasts column j of A and row j of Y through LDS, one
+//      barrier per step.  With d = A_jj (A after j steps), L_rj = A_rj / sqrt(d)
+//      and row j of Y is final once scaled by 1 / sqrt(d), so both rank-1 updates
+//      take the broadcast values times 1 / d, and L is never stored.
+//   2. M = Y^T Y with fp32 MFMA (32x32x2) from LDS; M goes to G and, in LDS, over Y.
+//   3. C = beta B M with B read from global memory and M from LDS.
 template <int D>
-__global__ __launch_bounds__(1024) void factor_kernel(float* __restrict__ G, float* __restrict__ Bm,
-                                                      const float* __restrict__ beta, int F, int H) {
+// (8 waves per SIMD caps a thread at 64 VGPRs; at d = 128 the compiler spills a
+// few loop-invariant values, and two workgroups per CU still run 1.5x faster
+// than one)
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void factor_kernel(float* __restrict__ G, float* __restrict__ Bm, const float* __restrict__ beta, int F, int H) {
   constexpr int TG = 32;          // thread grid side
   constexpr int NT = TG * TG;
   constexpr int RB = D / TG;
@@ -92,9 +98,9 @@ __global__ __launch_bounds__(1024) void factor_kernel(float* __restrict__ G, flo
   constexpr int NBLK = NB * NB;
   constexpr int PER_WAVE = (NBLK + NT / 64 - 1) / (NT / 64);
   extern __shared__ float sm[];
-  float* Ls = sm;                 // [D][LP]: L, later M
-  float* Xs = sm + D * LP;        // [D][LP]: Y, later B
-  float* cbuf = Xs + D * LP;      // [2][D]
+  float* Xs = sm;                 // [D][LP]: Y, later M
+  float* cbuf = Xs + D * LP;      // [2][D]: pivot column of A
+  float* rbuf = cbuf + 2 * D;     // [2][D]: pivot row of Y, before its scaling
 
   const int t = blockIdx.x + 1, h = blockIdx.y;
   const int tid = threadIdx.x, ty = tid / TG, tx = tid % TG;
@@ -103,93 +109,66 @@ __global__ __launch_bounds__(1024) void factor_kernel(float* __restrict__ G, flo
   float* Gp = G + ((size_t)t * H + h) * D * D;
   float* Bp = Bm + ((size_t)t * H + h) * D * D;
 
-  float a[RB][RB];
+  float a[RB][RB], y[RB][RB];
 #pragma unroll
   for (int ii = 0; ii < RB; ++ii)
 #pragma unroll
     for (int kk = 0; kk < RB; ++kk) {
       const int r = ty * RB + ii, c = tx * RB + kk;
       a[ii][kk] = b * Gp[r * D + c] + (r == c ? 1.f : 0.f);
+      y[ii][kk] = r == c ? 1.f : 0.f;
     }
 
-  // ---- 1. Cholesky
+  // ---- 1. Cholesky and L^-1, one column step at a time
   for (int jb = 0; jb < TG; ++jb) {
 #pragma unroll
     for (int jr = 0; jr < RB; ++jr) {
       const int jj = jb * RB + jr;
       float* cb = cbuf + (jj & 1) * D;
+      float* rv = rbuf + (jj & 1) * D;
       if (tx == jb) {
 #pragma unroll
         for (int ii = 0; ii < RB; ++ii) cb[ty * RB + ii] = a[ii][jr];
       }
+      if (ty == jb) {
+#pragma unroll
+        for (int kk = 0; kk < RB; ++kk) rv[tx * RB + kk] = y[jr][kk];
+      }
       __syncthreads();
       const float dj = cb[jj];
-      const float rsq = 1.f / sqrtf(dj);
       const float inv_d = 1.f / dj;
-      if (tx == jb) {
-#pragma unroll
-        for (int ii = 0; ii < RB; ++ii) {
-          const int i = ty * RB + ii;
-          Ls[i * LP + jj] = i >= jj ? cb[i] * rsq : 0.f;
-        }
-      }
-      float cr[RB], cc[RB];
+      const float rsq = 1.f / sqrtf(dj);
+      float cr[RB], cc[RB], yr[RB];
 #pragma unroll
       for (int x = 0; x < RB; ++x) {
-        cr[x] = cb[ty * RB + x];
+        cr[x] = cb[ty * RB + x] * inv_d;
         cc[x] = cb[tx * RB + x];
+        yr[x] = rv[tx * RB + x];
       }
-#pragma unroll
-      for (int ii = 0; ii < RB; ++ii)
-#pragma unroll
-        for (int kk = 0; kk < RB; ++kk) {
-          const int r = ty * RB + ii, c = tx * RB + kk;
-          if (r > jj && c > jj) a[ii][kk] -= cr[ii] * cc[kk] * inv_d;
-        }
-    }
-  }
-  __syncthreads();
-
-  // ---- 2. Y = L^-1 (reuse a[][] as Y)
-#pragma unroll
-  for (int ii = 0; ii < RB; ++ii)
-#pragma unroll
-    for (int kk = 0; kk < RB; ++kk) a[ii][kk] = (ty * RB + ii == tx * RB + kk) ? 1.f : 0.f;
-  for (int kb = 0; kb < TG; ++kb) {
-#pragma unroll
-    for (int kr = 0; kr < RB; ++kr) {
-      const int k = kb * RB + kr;
-      float* rb = cbuf + (k & 1) * D;
-      if (ty == kb) {
-        const float inv = 1.f / Ls[k * LP + k];
-#pragma unroll
-        for (int kk = 0; kk < RB; ++kk) {
-          a[kr][kk] *= inv;
-          rb[tx * RB + kk] = a[kr][kk];
-        }
-      }
-      __syncthreads();
-      float rv[RB];
-#pragma unroll
-      for (int kk = 0; kk < RB; ++kk) rv[kk] = rb[tx * RB + kk];
 #pragma unroll
       for (int ii = 0; ii < RB; ++ii) {
         const int r = ty * RB + ii;
-        if (r > k) {
-          const float l = Ls[r * LP + k];
+        if (r > jj) {
 #pragma unroll
-          for (int kk = 0; kk < RB; ++kk) a[ii][kk] -= l * rv[kk];
+          for (int kk = 0; kk < RB; ++kk) {
+            if (tx * RB + kk > jj) a[ii][kk] -= cr[ii] * cc[kk];
+            y[ii][kk] -= cr[ii] * yr[kk];
+          }
         }
+      }
+      if (ty == jb) {
+#pragma unroll
+        for (int kk = 0; kk < RB; ++kk) y[jr][kk] *= rsq;
       }
     }
   }
 #pragma unroll
   for (int ii = 0; ii < RB; ++ii)
 #pragma unroll
-    for (int kk = 0; kk < RB; ++kk) Xs[(ty * RB + ii) * LP + tx * RB + kk] = a[ii][kk];
+    for (int kk = 0; kk < RB; ++kk) Xs[(ty * RB + ii) * LP + tx * RB + kk] = y[ii][kk];
   __syncthreads();
 
-  // ---- 3a. M = Y^T Y  (M[a][b] = sum_k Y[k][a] Y[k][b])
+  // ---- 2. M = Y^T Y  (M[a][b] = sum_k Y[k][a] Y[k][b])
   floatx16 acc[PER_WAVE];
 #pragma unroll
   for (int x = 0; x < PER_WAVE; ++x) {
@@ -204,7 +183,7 @@ __global__ __launch_bounds__(1024) void factor_kernel(float* __restrict__ G, flo
       }
     }
   }
-  __syncthreads();   // Ls (L) and Xs (Y) reads done
+  __syncthreads();   // every read of Y done
 #pragma unroll
   for (int x = 0; x < PER_WAVE; ++x) {
     const int blk = w * PER_WAVE + x;
@@ -213,30 +192,37 @@ __global__ __launch_bounds__(1024) void factor_kernel(float* __restrict__ G, flo
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * ba + 8 * (r >> 2) + 4 * hf + (r & 3);
-        Ls[row * LP + 32 * bb + j] = acc[x][r];
+        Xs[row * LP + 32 * bb + j] = acc[x][r];
         Gp[row * D + 32 * bb + j] = acc[x][r];
       }
     }
   }
-  for (int e = tid; e < D * D; e += NT) Xs[(e / D) * LP + (e % D)] = Bp[e];
   __syncthreads();
 
-  // ---- 3b. C = beta B M  (C[a][b] = beta sum_k B[a][k] M[k][b])
+  // ---- 3. C = beta B M  (C[a][b] = beta sum_k B[a][k] M[k][b])
+#pragma unroll
+  for (int x = 0; x < PER_WAVE; ++x) {
+    const int blk = w * PER_WAVE + x;
+    acc[x] = floatx16{};
+    if (blk < NBLK) {
+      const int ba = blk / NB, bb = blk % NB;
+      for (int s = 0; s < D / 2; ++s) {
+        const float av = Bp[(32 * ba + j) * D + 2 * s + hf];
+        const float bv = Xs[(2 * s + hf) * LP + 32 * bb + j];
+        acc[x] = mfma_f32(av, bv, acc[x]);
+      }
+    }
+  }
+  __syncthreads();   // every read of B done before C overwrites it
 #pragma unroll
   for (int x = 0; x < PER_WAVE; ++x) {
     const int blk = w * PER_WAVE + x;
     if (blk < NBLK) {
       const int ba = blk / NB, bb = blk % NB;
-      floatx16 c = floatx16{};
-      for (int s = 0; s < D / 2; ++s) {
-        const float av = Xs[(32 * ba + j) * LP + 2 * s + hf];
-        const float bv = Ls[(2 * s + hf) * LP + 32 * bb + j];
-        c = mfma_f32(av, bv, c);
-      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * ba + 8 * (r >> 2) + 4 * hf + (r & 3);
-        Bp[row * D + 32 * bb + j] = b * c[r];
+        Bp[row * D + 32 * bb + j] = b * acc[x][r];
       }
     }
   }
@@ -527,7 +513,7 @@ hipError_t launch_gram_f32(const float* k, const float* v, int F, int N, int H, 
 
 template <int D>
 static hipError_t factor_d(float* G, float* B, const float* beta, int F, int H, hipStream_t st) {
-  const size_t lds = (2 * (size_t)D * (D + 1) + 2 * D) * sizeof(float);
+  const size_t lds = ((size_t)D * (D + 1) + 4 * D) * sizeof(float);
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&factor_kernel<D>),
