@@ -84,18 +84,29 @@ def tensor(name: str, F: int, N: int, H: int, d: int, seed: int = 0, q_std: floa
     if out is None:
         out = np.empty((len(frames), N, len(heads), d), dtype=np.float32)
 
-    def job(fi_hi):
+    def gen(fi_hi):
         fi, hi = fi_hi
-        b = block(name, frames[fi], heads[hi], N, d, seed, q_std)
-        if convert is not None:
-            b = convert(b)
-        out[fi, :, hi, :] = b
+        return block(name, frames[fi], heads[hi], N, d, seed, q_std)
 
-    work = [(fi, hi) for fi in range(len(frames)) for hi in range(len(heads))]
-    if len(work) * N * d < (1 << 22):
-        for w in work:
-            job(w)
+    nh = len(heads)
+    if len(frames) * nh * N * d < (1 << 22):
+        for fi in range(len(frames)):
+            for hi in range(nh):
+                b = gen((fi, hi))
+                out[fi, :, hi, :] = convert(b) if convert is not None else b
     else:
+        # worker threads only draw the float32 blocks (NumPy); `convert` and the
+        # stores into `out` (possibly torch calls, not safe to run from many
+        # threads at once) stay on the calling thread, one frame (all heads) per
+        # call, while the workers draw the next two frames
         with _cf.ThreadPoolExecutor(_workers()) as ex:
-            list(ex.map(job, work))
+            pending = {}
+            ahead = 2
+            for fi in range(min(ahead, len(frames))):
+                pending[fi] = [ex.submit(gen, (fi, hi)) for hi in range(nh)]
+            for fi in range(len(frames)):
+                if fi + ahead < len(frames):
+                    pending[fi + ahead] = [ex.submit(gen, (fi + ahead, hi)) for hi in range(nh)]
+                blk = np.stack([f.result() for f in pending.pop(fi)], axis=1)      # [N, heads, d]
+                out[fi] = convert(blk) if convert is not None else blk
     return out
