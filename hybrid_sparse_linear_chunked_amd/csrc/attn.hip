@@ -644,21 +644,24 @@ struct Item {
 __device__ inline Item decode_item(const AttnArgs& a) {
   Item it;
   const int F = a.F, N = a.N;
-  int bid;
-  {
-    const int G = gridDim.x, b = blockIdx.x;
-    const int x = b & 7, i8 = b >> 3, q8 = G >> 3, r8 = G & 7;
-    bid = (x < r8 ? x * (q8 + 1) : r8 * (q8 + 1) + (x - r8) * q8) + i8;
-  }
+  // Blocks go out head by head (all XCDs stream one head's K / V^T at a time,
+  // which the last-level cache holds); inside a head, the blocks one XCD receives
+  // (every 8th, as the dispatcher deals them round-robin) take a contiguous run of
+  // the head's items, so the items that share key frames share that XCD's L2.
+  const int na_h = a.na * a.qt_anchor * a.nsplit;        // anchor items per head
+  const int M = na_h + a.tiles_per_head;                 // items per head
+  const int b = blockIdx.x;
+  const int hh = b / M, p = b - hh * M;
+  const int q8 = M >> 3, m8 = M & 7, r = p & 7;
+  const int li = r * q8 + min(r, m8) + (p >> 3);         // item of head hh
   it.wf = it.we = it.k_f0 = 0;
-  if (bid < a.n_anchor_items) {
-    int r = bid;
-    const int qt = r % a.qt_anchor;
-    r /= a.qt_anchor;
-    it.anchor_idx = r % a.na;
-    r /= a.na;
-    it.split = r % a.nsplit;
-    it.h = r / a.nsplit;
+  if (li < na_h) {
+    int rr = li;
+    const int qt = rr % a.qt_anchor;
+    rr /= a.qt_anchor;
+    it.anchor_idx = rr % a.na;
+    it.split = rr / a.na;
+    it.h = hh;
     const int qf = it.anchor_idx == 0 ? 0 : F - 1;
     it.q_tok0 = qf * N + qt * a.bq;
     it.q_rows = min(a.bq, N - qt * a.bq);
@@ -666,21 +669,20 @@ __device__ inline Item decode_item(const AttnArgs& a) {
     it.k_f0 = it.split * a.fs;
     it.nslots = min(F, it.k_f0 + a.fs) - it.k_f0;
   } else {
-    int r = bid - a.n_anchor_items;
+    int rr = li - na_h;
     it.split = -1;
     it.anchor_idx = 0;
-    it.h = r / a.tiles_per_head;
-    r -= it.h * a.tiles_per_head;
+    it.h = hh;
     const int C = num_chunks(F);
     int c = 0;
     for (; c < C; ++c) {
       const int nf = nq_end(c, F) - nq_first(c);
       const int t = nf > 0 ? (nf * N + a.bq - 1) / a.bq : 0;
-      if (r < t) break;
-      r -= t;
+      if (rr < t) break;
+      rr -= t;
     }
     const int tok_begin = nq_first(c) * N, tok_end = nq_end(c, F) * N;
-    it.q_tok0 = tok_begin + r * a.bq;
+    it.q_tok0 = tok_begin + rr * a.bq;
     it.q_rows = min(a.bq, tok_end - it.q_tok0);
     it.mode = 1;
     it.wf = win_first(c);
