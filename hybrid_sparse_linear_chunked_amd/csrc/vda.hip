@@ -286,7 +286,16 @@ __global__ __launch_bounds__(2 * D) void scan_kernel(const float* __restrict__ M
 #pragma unroll
     for (int x = 0; x < MPER; ++x) mreg[x] = src[tid + NT * x];
   };
+  // C_t entries of this lane's outputs initialise the accumulator; like M_t they
+  // are loaded one step ahead
+  float4 creg[4];
+  auto load_c = [&](int t) {
+    const float* cp = Cg + (((size_t)t * H + h) * D + row) * D + 32 * w + 4 * hf;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) creg[g] = *reinterpret_cast<const float4*>(cp + 8 * g);
+  };
   load_m(t0);
+  load_c(t0);
   floatx16 acc = floatx16{};
   for (int step = 0; step < nsteps; ++step) {
     const int t = t0 + tstep * step;
@@ -299,20 +308,18 @@ __global__ __launch_bounds__(2 * D) void scan_kernel(const float* __restrict__ M
       Ms[r * LP + col + 2] = mreg[x].z;
       Ms[r * LP + col + 3] = mreg[x].w;
     }
-    // C_t entries of this lane's outputs initialise the accumulator
-    {
-      const float* cp = Cg + (((size_t)t * H + h) * D + row) * D + 32 * w + 4 * hf;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 cv = *reinterpret_cast<const float4*>(cp + 8 * g);
-        acc[4 * g + 0] = cv.x;
-        acc[4 * g + 1] = cv.y;
-        acc[4 * g + 2] = cv.z;
-        acc[4 * g + 3] = cv.w;
-      }
+    for (int g = 0; g < 4; ++g) {
+      acc[4 * g + 0] = creg[g].x;
+      acc[4 * g + 1] = creg[g].y;
+      acc[4 * g + 2] = creg[g].z;
+      acc[4 * g + 3] = creg[g].w;
     }
     __syncthreads();
-    if (step + 1 < nsteps) load_m(t + tstep);
+    if (step + 1 < nsteps) {
+      load_m(t + tstep);
+      load_c(t + tstep);
+    }
 #pragma unroll 8
     for (int s = 0; s < D / 2; ++s) {
       const int wb = s >> 4, e = s & 15;
