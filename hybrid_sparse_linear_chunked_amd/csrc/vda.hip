@@ -232,19 +232,18 @@ void factor_kernel(float* __restrict__ G, float* __restrict__ Bm, const float* _
 // grid (D/32 row blocks, 2 directions, H), D/32 waves.  Each workgroup carries
 // 32 rows of the state through every frame of its direction: the rows of
 // S <- S M + C evolve independently.  Wave w computes output columns
-// [32w, 32w+32) as S_new^T = M S^T + C^T with fp32 MFMA; the state is exchanged
-// between waves through LDS in the MFMA's own output layout.
+// [32w, 32w+32) as S_new^T = M S^T + C^T with fp32 MFMA (M is symmetric); its A
+// operand is rows 32w.. of M_t, which the wave reads from global memory into
+// registers one step ahead (no shared copy of M); the state goes between waves
+// through LDS in the MFMA's own output layout, double-buffered, one barrier per
+// step.
 template <int D>
 __global__ __launch_bounds__(2 * D) void scan_kernel(const float* __restrict__ Mg,
                                                      const float* __restrict__ Cg, int F, int H,
                                                      float* __restrict__ Sf, float* __restrict__ Sb) {
   constexpr int NW = D / 32;
-  constexpr int NT = 2 * D;                 // threads
-  constexpr int LP = D + 1;
-  constexpr int MCH = D * D / 4;            // float4 chunks of M
-  constexpr int MPER = MCH / NT;
-  __shared__ float Ms[D * LP];
-  __shared__ float Sx[NW * 16 * 64];
+  constexpr int NA = NW * 4;                // float4 pieces of this lane's A operand per step
+  __shared__ float Sx[2][NW * 16 * 64];
 
   const int rb = blockIdx.x, dir = blockIdx.y, h = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, j = lane & 31, hf = lane >> 5;
@@ -279,12 +278,14 @@ __global__ __launch_bounds__(2 * D) void scan_kernel(const float* __restrict__ M
   }
   if (nsteps <= 0) return;
 
-  for (int x = tid; x < NW * 16 * 64; x += NT) Sx[x] = 0.f;
-  float4 mreg[MPER];
-  auto load_m = [&](int t) {
-    const float4* src = reinterpret_cast<const float4*>(Mg + ((size_t)t * H + h) * D * D);
+  for (int x = threadIdx.x; x < NW * 16 * 64; x += 2 * D) Sx[0][x] = 0.f;
+  // lane (j, hf) of wave w feeds M[32w + j][32 wb + 8 g + 4 hf .. +3] for k-slots
+  // s = 16 wb + 4 g + 0..3 of the MFMA chain
+  float4 ma[NA], mn[NA];
+  auto load_m = [&](int t, float4* dst) {
+    const float* src = Mg + (((size_t)t * H + h) * D + 32 * w + j) * D + 4 * hf;
 #pragma unroll
-    for (int x = 0; x < MPER; ++x) mreg[x] = src[tid + NT * x];
+    for (int x = 0; x < NA; ++x) dst[x] = *reinterpret_cast<const float4*>(src + 32 * (x >> 2) + 8 * (x & 3));
   };
   // C_t entries of this lane's outputs initialise the accumulator; like M_t they
   // are loaded one step ahead
@@ -294,20 +295,14 @@ __global__ __launch_bounds__(2 * D) void scan_kernel(const float* __restrict__ M
 #pragma unroll
     for (int g = 0; g < 4; ++g) creg[g] = *reinterpret_cast<const float4*>(cp + 8 * g);
   };
-  load_m(t0);
+  load_m(t0, mn);
   load_c(t0);
+  __syncthreads();
   floatx16 acc = floatx16{};
   for (int step = 0; step < nsteps; ++step) {
-    const int t = t0 + tstep * step;
+    const int t = t0 + tstep * step, cur = step & 1;
 #pragma unroll
-    for (int x = 0; x < MPER; ++x) {
-      const int c4 = tid + NT * x;
-      const int r = (4 * c4) / D, col = (4 * c4) % D;
-      Ms[r * LP + col + 0] = mreg[x].x;
-      Ms[r * LP + col + 1] = mreg[x].y;
-      Ms[r * LP + col + 2] = mreg[x].z;
-      Ms[r * LP + col + 3] = mreg[x].w;
-    }
+    for (int x = 0; x < NA; ++x) ma[x] = mn[x];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       acc[4 * g + 0] = creg[g].x;
@@ -315,20 +310,22 @@ __global__ __launch_bounds__(2 * D) void scan_kernel(const float* __restrict__ M
       acc[4 * g + 2] = creg[g].z;
       acc[4 * g + 3] = creg[g].w;
     }
-    __syncthreads();
     if (step + 1 < nsteps) {
-      load_m(t + tstep);
+      load_m(t + tstep, mn);
       load_c(t + tstep);
     }
-#pragma unroll 8
+    const float* sx = Sx[cur];
+#pragma unroll
     for (int s = 0; s < D / 2; ++s) {
       const int wb = s >> 4, e = s & 15;
-      const int kap = 32 * wb + 8 * (e >> 2) + 4 * hf + (e & 3);
-      acc = mfma_f32(Ms[(32 * w + j) * LP + kap], Sx[(wb * 16 + e) * 64 + lane], acc);
+      const float4 m4 = ma[4 * wb + (e >> 2)];
+      const float av = (e & 3) == 0 ? m4.x : (e & 3) == 1 ? m4.y : (e & 3) == 2 ? m4.z : m4.w;
+      acc = mfma_f32(av, sx[(wb * 16 + e) * 64 + lane], acc);
     }
-    __syncthreads();
+    float* sxn = Sx[cur ^ 1];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) Sx[(w * 16 + e) * 64 + lane] = acc[e];
+    for (int e = 0; e < 16; ++e) sxn[(w * 16 + e) * 64 + lane] = acc[e];
+    __syncthreads();     // the new state is visible; every read of the old buffer is done
     if (dir == 0) {
       if (t % 5 == 4) {
         const int c = (t + 6) / 5;
