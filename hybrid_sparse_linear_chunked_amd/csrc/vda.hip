@@ -71,40 +71,50 @@ __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__
 }
 
 // ============================================================ per-frame affine maps
-// grid (F-2, H), 1024 threads (16 waves; two workgroups per CU, so 8 waves per
-// SIMD hide the latency of the serial column steps); frame t = blockIdx.x + 1.
+// grid (F-2, H), FACTOR_THREADS threads (9 waves; two workgroups per CU, 4-5
+// waves per SIMD hide the latency of the serial column steps); frame t =
+// blockIdx.x + 1.
 // In:  G = K K^T, B = V K^T of frame t.   Out (in place): G <- M = A^-1,
 // B <- C = beta B M, with A = I + beta G.
 //   1. Cholesky A = L L^T, right-looking, and in the same column steps Y = L^-1
-//      by right-looking forward substitution on the identity: both matrices live
-//      in registers (thread (ty, tx) of a 32 x 32 grid owns an RB x RB block of
-//      each); step j broadcasts column j of A and row j of Y through LDS, one
-//      barrier per step.  With d = A_jj (A after j steps), L_rj = A_rj / sqrt(d)
-//      and row j of Y is final once scaled by 1 / sqrt(d), so both rank-1 updates
-//      take the broadcast values times 1 / d, and L is never stored.
+//      by right-looking forward substitution on the identity.  Only lower
+//      triangles matter (A is symmetric, Y lower triangular), so thread i owns one
+//      RB x RB block (bi, bj), bi >= bj, of the 32 x 32 block grid, of A and of Y
+//      (528 blocks), in registers; step j broadcasts column j of A and row j of Y
+//      through LDS, one barrier per step.  With d = A_jj (A after j steps),
+//      L_rj = A_rj / sqrt(d) and row j of Y is final once scaled by 1 / sqrt(d), so
+//      both rank-1 updates take the broadcast values times 1 / d, and L is never
+//      stored.
 //   2. M = Y^T Y with fp32 MFMA (32x32x2) from LDS; M goes to G and, in LDS, over Y.
 //   3. C = beta B M with B read from global memory and M from LDS.
+constexpr int FACTOR_TG = 32;                                        // block grid side
+constexpr int FACTOR_NL = FACTOR_TG * (FACTOR_TG + 1) / 2;           // lower-triangle blocks
+constexpr int FACTOR_THREADS = (FACTOR_NL + 63) / 64 * 64;
 template <int D>
-// (8 waves per SIMD caps a thread at 64 VGPRs; at d = 128 the compiler spills a
-// few loop-invariant values, and two workgroups per CU still run 1.5x faster
-// than one)
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8)))
+__global__ __launch_bounds__(FACTOR_THREADS, 2)
 void factor_kernel(float* __restrict__ G, float* __restrict__ Bm, const float* __restrict__ beta, int F, int H) {
-  constexpr int TG = 32;          // thread grid side
-  constexpr int NT = TG * TG;
+  constexpr int TG = FACTOR_TG;
+  constexpr int NT = FACTOR_THREADS;
+  constexpr int NWV = NT / 64;
   constexpr int RB = D / TG;
   constexpr int LP = D + 1;
   constexpr int NB = D / 32;
   constexpr int NBLK = NB * NB;
-  constexpr int PER_WAVE = (NBLK + NT / 64 - 1) / (NT / 64);
+  constexpr int PER_WAVE = (NBLK + NWV - 1) / NWV;
   extern __shared__ float sm[];
   float* Xs = sm;                 // [D][LP]: Y, later M
   float* cbuf = Xs + D * LP;      // [2][D]: pivot column of A
   float* rbuf = cbuf + 2 * D;     // [2][D]: pivot row of Y, before its scaling
 
   const int t = blockIdx.x + 1, h = blockIdx.y;
-  const int tid = threadIdx.x, ty = tid / TG, tx = tid % TG;
+  const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, j = lane & 31, hf = lane >> 5;
+  // block (bi, bj) of this thread: tid = bi (bi + 1) / 2 + bj, 0 <= bj <= bi
+  const bool owns = tid < FACTOR_NL;
+  int bi = (int)((sqrtf(8.f * tid + 1.f) - 1.f) * 0.5f);
+  while (bi * (bi + 1) / 2 > tid) --bi;
+  while ((bi + 1) * (bi + 2) / 2 <= tid) ++bi;
+  const int bj = tid - bi * (bi + 1) / 2;
   const float b = beta[(size_t)t * H + h];
   float* Gp = G + ((size_t)t * H + h) * D * D;
   float* Bp = Bm + ((size_t)t * H + h) * D * D;
@@ -114,10 +124,11 @@ void factor_kernel(float* __restrict__ G, float* __restrict__ Bm, const float* _
   for (int ii = 0; ii < RB; ++ii)
 #pragma unroll
     for (int kk = 0; kk < RB; ++kk) {
-      const int r = ty * RB + ii, c = tx * RB + kk;
-      a[ii][kk] = b * Gp[r * D + c] + (r == c ? 1.f : 0.f);
+      const int r = bi * RB + ii, c = bj * RB + kk;
+      a[ii][kk] = owns ? b * Gp[r * D + c] + (r == c ? 1.f : 0.f) : 0.f;
       y[ii][kk] = r == c ? 1.f : 0.f;
     }
+  for (int x = tid; x < D * LP; x += NT) Xs[x] = 0.f;   // Y's upper triangle stays zero
 
   // ---- 1. Cholesky and L^-1, one column step at a time
   for (int jb = 0; jb < TG; ++jb) {
@@ -126,46 +137,50 @@ void factor_kernel(float* __restrict__ G, float* __restrict__ Bm, const float* _
       const int jj = jb * RB + jr;
       float* cb = cbuf + (jj & 1) * D;
       float* rv = rbuf + (jj & 1) * D;
-      if (tx == jb) {
+      if (owns && bj == jb) {
 #pragma unroll
-        for (int ii = 0; ii < RB; ++ii) cb[ty * RB + ii] = a[ii][jr];
+        for (int ii = 0; ii < RB; ++ii) cb[bi * RB + ii] = a[ii][jr];
       }
-      if (ty == jb) {
+      if (owns && bi == jb) {
 #pragma unroll
-        for (int kk = 0; kk < RB; ++kk) rv[tx * RB + kk] = y[jr][kk];
+        for (int kk = 0; kk < RB; ++kk) rv[bj * RB + kk] = y[jr][kk];
       }
       __syncthreads();
       const float dj = cb[jj];
       const float inv_d = 1.f / dj;
       const float rsq = 1.f / sqrtf(dj);
-      float cr[RB], cc[RB], yr[RB];
+      if (owns && bi >= jb) {
+        float cr[RB], cc[RB], yr[RB];
 #pragma unroll
-      for (int x = 0; x < RB; ++x) {
-        cr[x] = cb[ty * RB + x] * inv_d;
-        cc[x] = cb[tx * RB + x];
-        yr[x] = rv[tx * RB + x];
-      }
+        for (int x = 0; x < RB; ++x) {
+          cr[x] = cb[bi * RB + x] * inv_d;
+          cc[x] = cb[bj * RB + x];
+          yr[x] = bj <= jb ? rv[bj * RB + x] : 0.f;
+        }
 #pragma unroll
-      for (int ii = 0; ii < RB; ++ii) {
-        const int r = ty * RB + ii;
-        if (r > jj) {
+        for (int ii = 0; ii < RB; ++ii) {
+          const int r = bi * RB + ii;
+          if (r > jj) {
 #pragma unroll
-          for (int kk = 0; kk < RB; ++kk) {
-            if (tx * RB + kk > jj) a[ii][kk] -= cr[ii] * cc[kk];
-            y[ii][kk] -= cr[ii] * yr[kk];
+            for (int kk = 0; kk < RB; ++kk) {
+              if (bj * RB + kk > jj) a[ii][kk] -= cr[ii] * cc[kk];
+              y[ii][kk] -= cr[ii] * yr[kk];
+            }
           }
         }
-      }
-      if (ty == jb) {
+        if (bi == jb) {
 #pragma unroll
-        for (int kk = 0; kk < RB; ++kk) y[jr][kk] *= rsq;
+          for (int kk = 0; kk < RB; ++kk) y[jr][kk] *= rsq;
+        }
       }
     }
   }
+  if (owns) {
 #pragma unroll
-  for (int ii = 0; ii < RB; ++ii)
+    for (int ii = 0; ii < RB; ++ii)
 #pragma unroll
-    for (int kk = 0; kk < RB; ++kk) Xs[(ty * RB + ii) * LP + tx * RB + kk] = y[ii][kk];
+      for (int kk = 0; kk < RB; ++kk) Xs[(bi * RB + ii) * LP + bj * RB + kk] = y[ii][kk];
+  }
   __syncthreads();
 
   // ---- 2. M = Y^T Y  (M[a][b] = sum_k Y[k][a] Y[k][b])
@@ -525,7 +540,7 @@ static hipError_t factor_d(float* G, float* B, const float* beta, int F, int H, 
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(factor_kernel<D>, dim3(F - 2, H), dim3(1024), lds, st, G, B, beta, F, H);
+  hipLaunchKernelGGL(factor_kernel<D>, dim3(F - 2, H), dim3(FACTOR_THREADS), lds, st, G, B, beta, F, H);
   return hipGetLastError();
 }
 
