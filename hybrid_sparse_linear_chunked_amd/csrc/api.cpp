@@ -109,8 +109,10 @@ int check_ws(int F, int N, int H, int d, int prec, void* ws, size_t ws_bytes, La
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 // ---- pieces of the launch sequence
+// W: bf16 readout weights to fold into the attention epilogue (O = O_soft + W q on
+// the non-anchor frames), or null for O = O_soft
 int run_softmax(const void* q, const void* k, const void* v, int F, int N, int H, int d, int prec,
-                void* O, const Layout& L, WsPtr ws, bool vt_ready, hipStream_t st) {
+                void* O, const Layout& L, WsPtr ws, bool vt_ready, const uint16_t* W, hipStream_t st) {
   const uint8_t* q8 = nullptr;
   const uint8_t* k8 = nullptr;
   const float* amax = nullptr;
@@ -132,7 +134,7 @@ int run_softmax(const void* q, const void* k, const void* v, int F, int N, int H
   const int kprec = prec == VDN_PREC_FP32 ? 0 : (prec == VDN_PREC_BF16 ? 1 : 2);
   VDN_STAGE(VDN_STAGE_ATTN, st,
             vdn::launch_attn(kprec, q, k, v, ws.at<uint16_t>(L.vt), q8, k8, amax, F, N, H, d, O,
-                             ws.at<float>(L.pO), ws.at<float>(L.pml), st));
+                             ws.at<float>(L.pO), ws.at<float>(L.pml), W, st));
   VDN_STAGE(VDN_STAGE_COMBINE, st,
             vdn::launch_combine(prec == VDN_PREC_FP32 ? 0 : 1, ws.at<float>(L.pO), ws.at<float>(L.pml),
                                 F, N, H, d, O, st));
@@ -239,14 +241,18 @@ int vdn_hybrid_attn(const void* q, const void* k, const void* v, const float* be
   WsPtr ws{static_cast<unsigned char*>(workspace)};
   float* Sf = ws.at<float>(L.Sf);
   float* Sb = ws.at<float>(L.Sb);
-  // linear branch first: its pass over k and v also lays out v for the softmax branch
+  // linear branch first: its pass over k and v also lays out v for the softmax branch,
+  // and its readout weights are ready when the attention kernel ends its items
   if ((s = run_states(k, v, beta, F, N, H, d, precision, Sf, Sb, L, ws, st)) != VDN_OK) return s;
   const bool bf16 = precision != VDN_PREC_FP32;
   VDN_STAGE(VDN_STAGE_WPREP, st,
             vdn::launch_wprep(Sf, Sb, gate, vdn::num_chunks(F), H, d, bf16 ? 1 : 0, ws.at<void>(L.W), st));
-  if ((s = run_softmax(q, k, v, F, N, H, d, precision, O, L, ws, true, st)) != VDN_OK) return s;
-  VDN_STAGE(VDN_STAGE_READOUT, st,
-            vdn::launch_readout(bf16 ? 1 : 0, q, ws.at<void>(L.W), F, N, H, d, O, 1, st));
+  // bf16 / fp8: the readout and merge run in the attention kernel's epilogue;
+  // fp32: O_soft first, then the readout adds g (.) O_lin
+  const uint16_t* Wfused = bf16 ? ws.at<uint16_t>(L.W) : nullptr;
+  if ((s = run_softmax(q, k, v, F, N, H, d, precision, O, L, ws, true, Wfused, st)) != VDN_OK) return s;
+  if (!bf16)
+    VDN_STAGE(VDN_STAGE_READOUT, st, vdn::launch_readout(0, q, ws.at<void>(L.W), F, N, H, d, O, 1, st));
   return VDN_OK;
 }
 
@@ -260,7 +266,7 @@ int vdn_softmax_branch(const void* q, const void* k, const void* v, int F, int N
   Layout L;
   if ((s = check_ws(F, N, H, d, precision, workspace, workspace_bytes, &L)) != VDN_OK) return s;
   WsPtr ws{static_cast<unsigned char*>(workspace)};
-  return run_softmax(q, k, v, F, N, H, d, precision, O_soft, L, ws, false, as_stream(stream));
+  return run_softmax(q, k, v, F, N, H, d, precision, O_soft, L, ws, false, nullptr, as_stream(stream));
 }
 
 int vdn_vda_states(const void* k, const void* v, const float* beta, int F, int N, int H, int d,

@@ -179,6 +179,9 @@ struct AttnArgs {
   void* O;
   float* part_O;          // [nsplit][H][na][N][D]
   float* part_ml;         // [nsplit][H][na][N][2]
+  const uint16_t* W;      // bf16 / fp8 paths: readout weights g (.) (S_fwd + S_bwd), bf16
+                          // [C][H][D][D] (row = value dim); when set, chunk items write
+                          // O_soft + W q, else O_soft
   int F, N, H;
   int nsplit, fs, na, qt_anchor;
   int n_anchor_items;
@@ -709,7 +712,9 @@ __device__ inline Item uniform_item(Item it) {
 }
 
 template <int D, int PREC, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
+// (waves per SIMD: 2 at d = 128, which needs ~240 registers; the fp8 path at d = 64
+// fits 128 registers, i.e. two workgroups per CU)
+__global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_lds_kernel(AttnArgs a) {
   using Cfg = LdsCfg<D, PREC>;
   constexpr bool FP8 = Cfg::FP8;
   constexpr int NDB = D / 32;
@@ -983,6 +988,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; e += 2)
         psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[u & 1][e], pb[u & 1][e + 1]}, ones, psum, false);
+      // a fixed interleave: each MFMA followed by two exponentials and two other
+      // VALU ops (left to the scheduler, the order follows unrelated code elsewhere
+      // in the kernel, and some orders measured up to 3 % slower)
+#pragma unroll
+      for (int x = 0; x < NDB; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run += psum;
@@ -995,9 +1009,75 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
 
   // ---- epilogue
   const float l_tot = pair_sum(l_run);
+  // Linear-branch readout and gated merge, fused (besthub article "VDN-H3
+  // Generates 14-Second 768p Video ...", Hybrid Attention Architecture: the gated
+  // linear output is added to the softmax output): every query row of a chunk
+  // item lies in one chunk c, whose readout weights W = g (.) (S_fwd + S_bwd) come
+  // into the LDS stages (free since the last tile's barrier) by the same padded
+  // direct loads as a K tile; then O^T = O_soft^T + W Q^T with Q as the B operand
+  // it already is.  Anchor query frames (split items) take no linear term.
+  constexpr int WCH = D / 8;                         // 16-byte chunks per bf16 W row
+  constexpr int WP = 16 * (WCH + 1);                 // LDS pitch of a W row
+  constexpr int W_INSTR = (D * (WCH + 1) + 63) / 64; // wave-wide direct loads for W
+  static_assert(1024 * W_INSTR <= kLdsStages * Cfg::STAGE, "W fits in the LDS stages");
+  // The arguments only the epilogue needs (output pointers, readout weights) are
+  // read here, from the kernel's argument segment behind an empty asm statement,
+  // so that they are not loaded at entry and held in scalar registers through the
+  // tile loop.
+  using KArgs = const __attribute__((address_space(4))) AttnArgs*;
+  KArgs kargs = (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kargs));
+  const uint16_t* Wp = kargs->W;
+  const bool lin = it.split < 0 && Wp != nullptr;    // workgroup-uniform
+  if (lin) {
+    const int chunk = it.q_tok0 / N / kChunk;      // chunk of the item's first (and every) row
+    const uint16_t* wsrc = Wp + ((size_t)chunk * H + h) * (size_t)(D * D);
+    // rows past D (the last partial load at D = 32) read as zeros and are never used
+    const __amdgpu_buffer_rsrc_t wrsrc = make_rsrc(wsrc, (uint32_t)(D * D * 2));
+#pragma unroll
+    for (int x = 0; x < (W_INSTR + NW - 1) / NW; ++x) {
+      if (x * NW + w >= W_INSTR) break;
+      const int q = 64 * (x * NW + w) + lane;
+      const int row = q / (WCH + 1), c = min(q % (WCH + 1), WCH - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (lds_void_ptr)(smem + 1024 * (x * NW + w)), 16,
+                                               (uint32_t)(row * 2 * D + 16 * c), 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  // (all lanes take part in the MFMAs: lane j also supplies row j of W; rows of
+  // Q past the item's end are zeros)
+  float inv = 1.f / l_tot;
+  if (lin) {
+    // Q in bf16 as the B operand: the bf16 path's resident fragments carry the
+    // factor log2(e)/sqrt(d), taken back out of the product; the fp8 path reads q
+    constexpr int QS = D / 16;
+    bf16x8 qr[QS];
+    float us;
+    if constexpr (FP8) {
+      const uint16_t* q = static_cast<const uint16_t*>(a.q);
+#pragma unroll
+      for (int s = 0; s < QS; ++s)
+        qr[s] = qvalid ? *reinterpret_cast<const bf16x8*>(q + qoff + 16 * s + 8 * hf) : bf16x8{};
+      us = 1.f;
+    } else {
+#pragma unroll
+      for (int s = 0; s < QS; ++s) qr[s] = qb[s];
+      us = 1.f / kargs->scale_log2;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      floatx16 acc = floatx16{};
+#pragma unroll
+      for (int s = 0; s < QS; ++s)
+        acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(smem + (32 * db + j) * WP + 16 * (2 * s + hf)), qr[s], acc);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = fmaf(acc[r], us, o[db][r] * inv);
+    }
+    inv = 1.f;
+  }
   if (!qvalid) return;
   if (it.split < 0) {
-    const float inv = 1.f / l_tot;
     const size_t ooff = (size_t)(it.q_tok0 + qi) * rs + (size_t)h * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -1006,12 +1086,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
         const int dd = 32 * db + 8 * g + 4 * hf;
         const uint2 pk = make_uint2(pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
                                     pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.O) + ooff + dd) = pk;
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(kargs->O) + ooff + dd) = pk;
       }
   } else {
     const int n = it.q_tok0 - (it.anchor_idx == 0 ? 0 : (F - 1) * N) + qi;
-    const size_t row = (((size_t)it.split * H + h) * a.na + it.anchor_idx) * N + n;
-    float* po = a.part_O + row * D;
+    const size_t row = (((size_t)it.split * H + h) * kargs->na + it.anchor_idx) * N + n;
+    float* po = kargs->part_O + row * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -1021,8 +1101,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
             make_float4(o[db][4 * g + 0], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
       }
     if (hf == 0) {
-      a.part_ml[2 * row + 0] = m_run;
-      a.part_ml[2 * row + 1] = l_tot;
+      kargs->part_ml[2 * row + 0] = m_run;
+      kargs->part_ml[2 * row + 1] = l_tot;
     }
   }
 }
@@ -1218,10 +1298,13 @@ static hipError_t attn_lds(const AttnArgs& a, hipStream_t st) {
 
 hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, const uint16_t* vt,
                        const uint8_t* q8, const uint8_t* k8, const float* amax, int F, int N, int H,
-                       int D, void* O, float* part_O, float* part_ml, hipStream_t st) {
+                       int D, void* O, float* part_O, float* part_ml, const uint16_t* W,
+                       hipStream_t st) {
   AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.vt = vt; a.q8 = q8; a.k8 = k8; a.amax = amax;
   a.O = O; a.part_O = part_O; a.part_ml = part_ml;
+  a.W = W;
+  if (prec == 0 && W != nullptr) return hipErrorInvalidValue;   // the fp32 kernel has no fused readout
   a.F = F; a.N = N; a.H = H;
   attn_split_plan(F, &a.nsplit, &a.fs);
   a.na = F >= 2 ? 2 : 1;

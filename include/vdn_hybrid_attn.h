@@ -74,7 +74,10 @@ size_t vdn_workspace_bytes(int F, int N, int H, int d, int precision);
 /* The whole hybrid layer: O = O_soft + g (.) O_lin.
  * Cited definition: see the header comment (all three parts).
  * q, k, v, O: [F, N, H, d]; beta: [F, H] (beta_t > 0 for a meaningful update);
- * gate: [H, d].  O must not alias q, k or v. */
+ * gate: [H, d].  O must not alias q, k or v.  With bf16 I/O the readout and
+ * merge run in the softmax kernel's epilogue: O is written once, as the bf16
+ * rounding of O_soft + g (.) O_lin (fp32: O_soft is written, then the readout adds
+ * g (.) O_lin to it). */
 int vdn_hybrid_attn(const void* q, const void* k, const void* v,
                     const float* beta, const float* gate,
                     int F, int N, int H, int d, int precision,
@@ -132,9 +135,11 @@ int vdn_schedule(int F, int* table, int cap);
 #define VDN_STAGE_FACTOR   1   /* per-frame Cholesky: M_t = A_t^-1, C_t = beta B_t M_t     */
 #define VDN_STAGE_SCAN     2   /* serial state scan, both directions                     */
 #define VDN_STAGE_WPREP    3   /* readout weights g (.) (S_fwd + S_bwd)                   */
-#define VDN_STAGE_ATTN     4   /* windowed + anchored softmax attention                  */
+#define VDN_STAGE_ATTN     4   /* windowed + anchored softmax attention (bf16 I/O layer:
+                                  with the readout + gated merge in its epilogue)       */
 #define VDN_STAGE_COMBINE  5   /* merge of the anchor rows' key slices                   */
-#define VDN_STAGE_READOUT  6   /* linear readout + gated merge                           */
+#define VDN_STAGE_READOUT  6   /* linear readout (+ gated merge in the fp32 layer; the
+                                  readout of vdn_vda_linear)                            */
 #define VDN_STAGE_QUANT    7   /* fp8 quantiser of q and k                               */
 #define VDN_NUM_STAGES     8
 

@@ -102,6 +102,8 @@ def test_small_configs_full(cfg):
     (16, 24, 3, 32, "fp32"),
     (26, 65, 2, 128, "fp32"),
     (31, 48, 2, 64, "bf16_fp8qk"),
+    (23, 37, 3, 32, "bf16"),      # d = 32 with linear states: partial load of the readout weights
+    (24, 50, 2, 128, "bf16_fp8qk"),
 ])
 def test_edge_shapes(cfg):
     F, N, H, d, prec = cfg
