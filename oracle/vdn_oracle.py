@@ -24,7 +24,10 @@ It computes, in float64 with NumPy, exactly what the layer is defined to compute
     and the results are added) [sd114.wiki section 双向线性注意力分支];
   * the gated merge O = O_soft + g * O_lin [arXiv abstract: separate output
     projections and learnable gates calibrate the two branches; besthub section
-    Hybrid Attention Architecture: outputs merged by a gating mechanism].
+    Hybrid Attention Architecture: outputs merged by a gating mechanism];
+  * with extra (text / audio) tokens in the layer, plain softmax for every
+    interaction that involves one of them [arXiv abstract; ananclaw note,
+    section 一、方法拆解].
 
 Tensor layout: q, k, v are [F, N, H, d] (frame, token-in-frame, head, channel);
 beta is [F, H]; gate is [H, d]; states are [C, H, d, d] with C = ceil(F / 5),
@@ -264,6 +267,109 @@ def hybrid(q, k, v, beta, gate, dense=False):
     S_fwd, S_bwd = vda_states(k, v, beta)
     O_lin = linear_branch(q, S_fwd, S_bwd)
     return merge(O_soft, O_lin, gate), O_soft, O_lin
+
+
+# --------------------------------------------------------------------------
+# Extra (text / audio) tokens in the same layer
+# --------------------------------------------------------------------------
+# The hybrid replaces only video-to-video interactions; every interaction that
+# involves a text or audio token stays plain softmax [arXiv abstract page, Abstract;
+# ananclaw note, section 一、方法拆解].  With T such tokens (qx, kx, vx: [T, H, d]):
+#   * a video query of frame i attends, in one softmax, to the tokens of its key
+#     frames S(i) and to all T extra tokens;
+#   * an extra query attends to every video token and every extra token;
+#   * the linear branch and the merge concern video tokens only; an extra token's
+#     output is its softmax output.
+
+def softmax_branch_mixed(q, k, v, kx, vx, frames=None, heads=None, tokens=None) -> np.ndarray:
+    """Video query rows of the softmax branch with extra key tokens.
+
+    Same return layout as softmax_branch; kx, vx: [T, H, d]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    kx = np.asarray(kx, dtype=np.float64)
+    vx = np.asarray(vx, dtype=np.float64)
+    F, N, H, d = q.shape
+    frames = list(range(F)) if frames is None else list(frames)
+    heads = list(range(H)) if heads is None else list(heads)
+    tokens = list(range(N)) if tokens is None else list(tokens)
+    out = np.zeros((len(frames), len(tokens), len(heads), d))
+    for a, h in enumerate(heads):
+        for b, i in enumerate(frames):
+            keys = np.concatenate([k[j, :, h, :] for j in softmax_frames(i, F)] + [kx[:, h, :]], axis=0)
+            vals = np.concatenate([v[j, :, h, :] for j in softmax_frames(i, F)] + [vx[:, h, :]], axis=0)
+            p = _softmax_rows(q[i, tokens, h, :] @ keys.T / math.sqrt(d))
+            out[b, :, a, :] = p @ vals
+    return out
+
+
+def softmax_extra_rows(k, v, qx, kx, vx, heads=None, xtokens=None) -> np.ndarray:
+    """Extra query rows: softmax over all F*N video tokens and all T extra tokens.
+
+    Returns float64 [len(xtokens), len(heads), d]."""
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    qx = np.asarray(qx, dtype=np.float64)
+    kx = np.asarray(kx, dtype=np.float64)
+    vx = np.asarray(vx, dtype=np.float64)
+    F, N, H, d = k.shape
+    T = qx.shape[0]
+    heads = list(range(H)) if heads is None else list(heads)
+    xtokens = list(range(T)) if xtokens is None else list(xtokens)
+    out = np.zeros((len(xtokens), len(heads), d))
+    for a, h in enumerate(heads):
+        keys = np.concatenate([k[:, :, h, :].reshape(F * N, d), kx[:, h, :]], axis=0)
+        vals = np.concatenate([v[:, :, h, :].reshape(F * N, d), vx[:, h, :]], axis=0)
+        p = _softmax_rows(qx[xtokens, h, :] @ keys.T / math.sqrt(d))
+        out[:, a, :] = p @ vals
+    return out
+
+
+def token_mask_mixed(F: int, N: int, T: int) -> np.ndarray:
+    """Boolean [F*N+T, F*N+T] over video tokens (frame-major) then extra tokens:
+    video-video entries follow frame_mask, every entry in an extra row or column
+    is True."""
+    L = F * N
+    m = np.ones((L + T, L + T), dtype=bool)
+    m[:L, :L] = np.kron(frame_mask(F), np.ones((N, N), dtype=bool)).astype(bool)
+    return m
+
+
+def softmax_mixed_dense(q, k, v, qx, kx, vx):
+    """Both kinds of rows as one dense attention over F*N+T tokens under
+    token_mask_mixed (small inputs only).  Returns (O_video [F, N, H, d],
+    O_extra [T, H, d])."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    F, N, H, d = q.shape
+    T = np.asarray(qx).shape[0]
+    mask = token_mask_mixed(F, N, T)
+    ov = np.zeros_like(q)
+    ox = np.zeros((T, H, d))
+    for h in range(H):
+        Q = np.concatenate([q[:, :, h, :].reshape(F * N, d), np.asarray(qx, np.float64)[:, h, :]], axis=0)
+        K = np.concatenate([k[:, :, h, :].reshape(F * N, d), np.asarray(kx, np.float64)[:, h, :]], axis=0)
+        V = np.concatenate([v[:, :, h, :].reshape(F * N, d), np.asarray(vx, np.float64)[:, h, :]], axis=0)
+        s = np.where(mask, Q @ K.T / math.sqrt(d), -np.inf)
+        o = _softmax_rows(s) @ V
+        ov[:, :, h, :] = o[:F * N].reshape(F, N, d)
+        ox[:, h, :] = o[F * N:]
+    return ov, ox
+
+
+def hybrid_mixed(q, k, v, qx, kx, vx, beta, gate, dense=False):
+    """The layer with T extra tokens.  Returns (O_video, O_extra, O_soft_video,
+    O_lin): video rows O = O_soft + g * O_lin, extra rows their softmax output."""
+    if dense:
+        O_soft, O_x = softmax_mixed_dense(q, k, v, qx, kx, vx)
+    else:
+        O_soft = softmax_branch_mixed(q, k, v, kx, vx)
+        O_x = softmax_extra_rows(k, v, qx, kx, vx)
+    S_fwd, S_bwd = vda_states(k, v, beta)
+    O_lin = linear_branch(q, S_fwd, S_bwd)
+    return merge(O_soft, O_lin, gate), O_x, O_soft, O_lin
 
 
 # --------------------------------------------------------------------------

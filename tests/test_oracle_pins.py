@@ -127,6 +127,88 @@ def test_zero_query_gives_mean_of_visible_values():
         np.testing.assert_allclose(out[i], np.broadcast_to(ref, (N, H, d)), rtol=1e-12, atol=1e-13)
 
 
+# ---------------------------------------------------------------- extra (text / audio) tokens
+
+def small_extra(T, H, d, seed=0, q_std=1.0):
+    return tuple(vdn_synth.extra(n, T, H, d, seed=seed, q_std=q_std).astype(np.float64)
+                 for n in ("q", "k", "v"))
+
+
+@pytest.mark.parametrize("F,T", [(1, 3), (4, 5), (10, 7)])
+def test_short_video_with_extras_is_full_attention(F, T):
+    # F <= 10: the video part is full attention, and extra tokens add plain softmax
+    # keys and rows, so the whole branch is unmasked attention over F*N+T tokens.
+    N, H, d = 5, 2, 8
+    q, k, v = small_inputs(F, N, H, d, seed=F)
+    qx, kx, vx = small_extra(T, H, d, seed=F)
+    ov = orc.softmax_branch_mixed(q, k, v, kx, vx)
+    ox = orc.softmax_extra_rows(k, v, qx, kx, vx)
+    dv, dx = orc.softmax_mixed_dense(q, k, v, qx, kx, vx)
+    for h in range(H):
+        cat = lambda a, ax: np.concatenate([a[:, :, h].reshape(-1, d), ax[:, h]], axis=0)
+        ref = _sdpa(cat(q, qx), cat(k, kx), cat(v, vx))
+        for got_v, got_x in ((ov, ox), (dv, dx)):
+            np.testing.assert_allclose(got_v[:, :, h].reshape(-1, d), ref[:F * N], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(got_x[:, h], ref[F * N:], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("F,T", [(20, 6), (22, 9)])
+def test_mixed_softmax_equals_masked_sdpa(F, T):
+    # the hand-written frame table for video-video pairs, every pair with an extra
+    # token allowed
+    N, H, d = 3, 2, 8
+    q, k, v = small_inputs(F, N, H, d, seed=3, q_std=4.0)
+    qx, kx, vx = small_extra(T, H, d, seed=3, q_std=4.0)
+    table = load_partition(F)
+    fmask = np.zeros((F, F), dtype=bool)
+    for i in range(F):
+        fmask[i, table[i][0]] = True
+    tmask = np.ones((F * N + T, F * N + T), dtype=bool)
+    tmask[:F * N, :F * N] = np.kron(fmask, np.ones((N, N), dtype=bool))
+    ov = orc.softmax_branch_mixed(q, k, v, kx, vx)
+    ox = orc.softmax_extra_rows(k, v, qx, kx, vx)
+    dv, dx = orc.softmax_mixed_dense(q, k, v, qx, kx, vx)
+    for h in range(H):
+        cat = lambda a, ax: np.concatenate([a[:, :, h].reshape(-1, d), ax[:, h]], axis=0)
+        ref = _sdpa(cat(q, qx), cat(k, kx), cat(v, vx), tmask)
+        for got_v, got_x in ((ov, ox), (dv, dx)):
+            np.testing.assert_allclose(got_v[:, :, h].reshape(-1, d), ref[:F * N], rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(got_x[:, h], ref[F * N:], rtol=1e-11, atol=1e-12)
+
+
+def test_mixed_zero_query_gives_mean_of_visible_values():
+    # q = 0: a video row of frame i averages v over its table frames and all extra
+    # tokens; an extra row averages v over every token
+    F, N, T, H, d = 20, 4, 6, 2, 8
+    _, k, v = small_inputs(F, N, H, d, seed=4)
+    _, kx, vx = small_extra(T, H, d, seed=4)
+    ov = orc.softmax_branch_mixed(np.zeros_like(k), k, v, kx, vx)
+    ox = orc.softmax_extra_rows(k, v, np.zeros_like(kx), kx, vx)
+    table = load_partition(F)
+    for i in range(F):
+        vis = np.concatenate([v[table[i][0]].reshape(-1, H, d), vx], axis=0)
+        np.testing.assert_allclose(ov[i], np.broadcast_to(vis.mean(axis=0), (N, H, d)), rtol=1e-12, atol=1e-13)
+    allv = np.concatenate([v.reshape(-1, H, d), vx], axis=0).mean(axis=0)
+    np.testing.assert_allclose(ox, np.broadcast_to(allv, (T, H, d)), rtol=1e-12, atol=1e-13)
+
+
+def test_mixed_layer_linear_branch_is_video_only():
+    # extra tokens change neither the states nor O_lin, and with T = 0 the mixed
+    # layer is the video layer
+    F, N, T, H, d = 22, 3, 4, 2, 8
+    q, k, v = small_inputs(F, N, H, d, seed=5)
+    qx, kx, vx = small_extra(T, H, d, seed=5)
+    beta, gate = vdn_synth.beta(F, H, seed=5), vdn_synth.gate(H, d, seed=5)
+    O, Ox, Os, Ol = orc.hybrid_mixed(q, k, v, qx, kx, vx, beta, gate)
+    O0, Os0, Ol0 = orc.hybrid(q, k, v, beta, gate)
+    np.testing.assert_array_equal(Ol, Ol0)
+    np.testing.assert_allclose(O - Os, O0 - Os0, rtol=1e-12, atol=1e-12)
+    e = np.zeros((0, H, d))
+    Oe, Oxe, Ose, _ = orc.hybrid_mixed(q, k, v, e, e, e, beta, gate)
+    np.testing.assert_allclose(Oe, O0, rtol=1e-12, atol=1e-13)
+    assert Oxe.shape == (0, H, d)
+
+
 # ---------------------------------------------------------------- VDA update
 
 def test_update_is_least_squares_minimiser():

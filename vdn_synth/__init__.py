@@ -12,7 +12,10 @@ Recipe (every configuration):
   * beta ~ U(0.2, 0.8) per (frame, head) from SeedSequence([seed, 3]);
   * gate = sigmoid(N(0, 1)) per (head, channel) from SeedSequence([seed, 4]);
   * q_std scales q (the "sharp" variant uses q_std = 4 * sqrt(d), which puts the
-    attention logits at standard deviation ~4).
+    attention logits at standard deviation ~4);
+  * extra (text / audio) tokens, when a layer has them: q, k, v of T tokens, the
+    same distributions, one T x d block per (tensor, head) from
+    SeedSequence([seed, 5 + tensor_id, head]), laid out [T, H, d].
 
 Block seeding lets a test regenerate only the frames and heads it samples.
 Tensors are laid out [F, N, H, d] (token-major, one token = H*d contiguous values).
@@ -50,6 +53,20 @@ def block(name: str, frame: int, head: int, N: int, d: int, seed: int = 0,
     elif name == "q" and q_std != 1.0:
         x = x * np.float32(q_std)
     return x
+
+
+def extra(name: str, T: int, H: int, d: int, seed: int = 0, q_std: float = 1.0) -> np.ndarray:
+    """q, k or v of T extra tokens: float32 [T, H, d]."""
+    out = np.empty((T, H, d), dtype=np.float32)
+    for h in range(H):
+        x = _rng(seed, 5 + TENSOR_ID[name], h).standard_normal((T, d), dtype=np.float32)
+        if name == "k":
+            nrm = np.sqrt(np.sum(x * x, axis=1, dtype=np.float32), dtype=np.float32)
+            x = x / nrm[:, None]
+        elif name == "q" and q_std != 1.0:
+            x = x * np.float32(q_std)
+        out[:, h, :] = x
+    return out
 
 
 def beta(F: int, H: int, seed: int = 0) -> np.ndarray:
