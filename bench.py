@@ -8,7 +8,8 @@ over one batch of seeded synthetic inputs already resident in HBM.
 
 Default workload: F=90 latent frames x N=4032 tokens (48 x 84 patches), H=24,
 d=128, bf16 -- the 768p / 14.4 s shaped layer.  `--config 4` runs the F=180
-fp8-q.k variant instead.
+fp8-q.k variant instead; `--extra-tokens T` appends T text / audio tokens to the
+sequence (plain softmax for every interaction involving them).
 
 Prints ONE JSON line.  Besides the contract fields it carries
   roofline      dominant kernel (softmax attention + fused readout): algorithmic
@@ -54,11 +55,13 @@ def frame_pairs(F):
     return P
 
 
-def algorithmic_work(F, N, H, d):
-    """FLOP of each part of the method (not of dense attention) and readout bytes."""
+def algorithmic_work(F, N, H, d, T=0):
+    """FLOP of each part of the method (not of dense attention) and readout bytes;
+    T extra tokens add video x extra and extra x all softmax pairs."""
     P = frame_pairs(F)
     C = (F + 4) // 5
     soft = 4.0 * d * H * N * N * P                  # Q.K^T and P.V over visited pairs
+    soft += 4.0 * d * H * T * (2.0 * F * N + T)     # with extra tokens
     grams = 4.0 * d * d * N * max(F - 2, 0) * H     # K K^T and V K^T per non-anchor frame
     scan = 2.0 * H * max(F - 11, 0) * (7.0 / 3.0) * d ** 3
     readout = 2.0 * d * d * max(F - 2, 0) * N * H
@@ -155,6 +158,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=3, choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra-tokens", type=int, default=0, metavar="T",
+                    help="append T text / audio tokens to the layer's sequence (no CPU baseline)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (a known-size kernel "
                          "that calibrates the HBM byte counters), then exit")
@@ -184,23 +189,34 @@ def main():
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
 
+    T = args.extra_tokens
+
     def gen(name):
         out = torch.empty((F, N, H, d), dtype=torch.bfloat16)
         vdn_synth.tensor(name, F, N, H, d, out=out,
                          convert=lambda b: torch.from_numpy(b).to(torch.bfloat16))
+        if T > 0:
+            ext = torch.from_numpy(vdn_synth.extra(name, T, H, d)).to(torch.bfloat16)
+            out = torch.cat([out.reshape(F * N, H, d), ext], dim=0)
         return out.to(dev)
 
     q, k, v = gen("q"), gen("k"), gen("v")
     beta = torch.from_numpy(vdn_synth.beta(F, H)).to(dev)
     gate = torch.from_numpy(vdn_synth.gate(H, d)).to(dev)
     O = torch.empty_like(q)
-    ws = vdn.new_workspace(F, N, H, d, p, device=dev)
+    ws = (vdn.new_workspace_mixed(F, N, T, H, d, p, device=dev) if T > 0
+          else vdn.new_workspace(F, N, H, d, p, device=dev))
+    # the video tokens as [F, N, H, d] (the first F*N tokens when there are extras)
+    qv, kv, vv = (x[:F * N].view(F, N, H, d) for x in (q, k, v)) if T > 0 else (q, k, v)
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; workspace "
           f"{ws.numel() / 2**30:.2f} GiB", file=sys.stderr, flush=True)
 
     def step():
-        vdn.hybrid_attn(q, k, v, beta, gate, precision=p, out=O, workspace=ws)
+        if T > 0:
+            vdn.hybrid_attn_mixed(q, k, v, beta, gate, F, N, precision=p, out=O, workspace=ws)
+        else:
+            vdn.hybrid_attn(q, k, v, beta, gate, precision=p, out=O, workspace=ws)
 
     for i in range(args.warmup):
         step()
@@ -239,7 +255,7 @@ def main():
     print(f"[bench] {args.steps} steps: {ms:.2f} ms/step (wall {1000 * wall / args.steps:.2f})",
           file=sys.stderr, flush=True)
 
-    work = algorithmic_work(F, N, H, d)
+    work = algorithmic_work(F, N, H, d, T)
     attn_ms = stages["attn"]
     kflop = work["soft"] + work["readout"]      # softmax branch + the fused W q
     if prec == "bf16_fp8qk":
@@ -250,19 +266,19 @@ def main():
         peak = PEAK_BF16_TFLOPS
     achieved = kflop / (attn_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.config),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": measured_traffic(args.config) if T == 0 else None,
                 "kernel": "attn_lds_kernel", "flop_per_launch": kflop, "kernel_ms": round(attn_ms, 3)}
 
     # the readout kernel on its own, for its HBM roofline (outside the timed layer)
     ro_st = vdn.STAGES.index("readout")
-    Sf, Sb = vdn.vda_states(k, v, beta, precision=p, workspace=ws)
+    Sf, Sb = vdn.vda_states(kv, vv, beta, precision=p, workspace=ws)
     ro_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(6)]
     for e0, e1 in ro_ev:           # torch creates the HIP event on its first record
         e0.record()
         e1.record()
     for e0, e1 in ro_ev:
         vdn.set_stage_events(ro_st, e0, e1)
-        O_lin = vdn.vda_linear(q, Sf, Sb, precision=p, workspace=ws)
+        O_lin = vdn.vda_linear(qv, Sf, Sb, precision=p, workspace=ws)
         del O_lin
     vdn.set_stage_events(ro_st, None, None)
     torch.cuda.synchronize()
@@ -279,15 +295,15 @@ def main():
         "metric": METRIC, "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg["workload"], "F": F, "N": N, "H": H, "d": d, "precision": prec,
-                   "frame_pairs": work["P"]},
+        "config": {"workload": cfg["workload"] + (f"_with_{T}_text_tokens" if T else ""), "F": F, "N": N,
+                   "H": H, "d": d, "precision": prec, "frame_pairs": work["P"], "extra_tokens": T},
         "tflops": round(work["total"] / (ms * 1e-3) / 1e12, 2),
         "layer_flop": work["total"],
         "roofline": roofline,
         "readout": readout,
         "stages_ms": {k2: round(v2, 4) for k2, v2 in stages.items()},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and T == 0:
         print("[bench] timing the oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(F, N, H, d)
     print(json.dumps(result), flush=True)

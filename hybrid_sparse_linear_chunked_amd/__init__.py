@@ -30,6 +30,8 @@ _SZ = ctypes.c_size_t
 _SIGS = {
     "vdn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "vdn_hybrid_attn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "vdn_workspace_bytes_mixed": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "vdn_hybrid_attn_mixed": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "vdn_softmax_branch": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "vdn_vda_states": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "vdn_vda_linear": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
@@ -90,6 +92,10 @@ def schedule(F: int) -> np.ndarray:
 
 def workspace_bytes(F: int, N: int, H: int, d: int, precision: int) -> int:
     return int(load().vdn_workspace_bytes(F, N, H, d, precision))
+
+
+def workspace_bytes_mixed(F: int, N: int, T: int, H: int, d: int, precision: int) -> int:
+    return int(load().vdn_workspace_bytes_mixed(F, N, T, H, d, precision))
 
 
 # ------------------------------------------------------------------ torch side
@@ -160,6 +166,46 @@ def hybrid_attn(q, k, v, beta, gate, precision=None, out=None, workspace=None):
                                 gate.data_ptr(), F, N, H, d, prec, O.data_ptr(), ws.data_ptr(),
                                 ws.numel(), _stream())
     _check(st, "vdn_hybrid_attn")
+    return O
+
+
+def new_workspace_mixed(F, N, T, H, d, precision, device="cuda"):
+    """A workspace tensor for repeated hybrid_attn_mixed calls with this shape."""
+    prec = precision if isinstance(precision, int) else PRECISIONS[precision]
+    need = workspace_bytes_mixed(F, N, T, H, d, prec)
+    if need == 0:
+        raise VdnError(ERR_UNSUPPORTED, "vdn_workspace_bytes_mixed")
+    return _torch().empty(need, dtype=_torch().uint8, device=device)
+
+
+def hybrid_attn_mixed(q, k, v, beta, gate, F, N, precision=None, out=None, workspace=None):
+    """The layer with extra (text / audio) tokens: q, k, v [F*N + T, H, d], the
+    F*N video tokens (frame-major) then T extra tokens; beta fp32 [F, H]; gate fp32
+    [H, d].  Returns O of q's shape."""
+    torch = _torch()
+    prec = _precision_of(q, precision)
+    L, H, d = q.shape
+    T = L - F * N
+    if T < 0:
+        raise ValueError(f"q has {L} tokens, fewer than F*N = {F * N}")
+    dt = _io_dtype(prec)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_io(name, x, dt, (L, H, d))
+    _check_io("beta", beta, torch.float32, (F, H))
+    _check_io("gate", gate, torch.float32, (H, d))
+    O = torch.empty_like(q) if out is None else out
+    _check_io("out", O, dt, (L, H, d))
+    need = workspace_bytes_mixed(F, N, T, H, d, prec)
+    if need == 0:
+        raise VdnError(ERR_UNSUPPORTED, "vdn_workspace_bytes_mixed")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise VdnError(ERR_WORKSPACE, "workspace")
+    st = load().vdn_hybrid_attn_mixed(q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+                                      gate.data_ptr(), F, N, T, H, d, prec, O.data_ptr(),
+                                      workspace.data_ptr(), workspace.numel(), _stream())
+    _check(st, "vdn_hybrid_attn_mixed")
     return O
 
 

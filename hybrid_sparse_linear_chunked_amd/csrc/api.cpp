@@ -55,13 +55,22 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Extra (text / audio) tokens: bf16 / fp8 only; every token index stays 32-bit.
+int check_extra(int F, int N, int T, int prec) {
+  if (T < 0) return VDN_ERR_INVALID_ARG;
+  if (T > 0 && prec == VDN_PREC_FP32) return VDN_ERR_UNSUPPORTED;
+  if (static_cast<long long>(F) * N + T > (1LL << 30)) return VDN_ERR_UNSUPPORTED;
+  return VDN_OK;
+}
+
 // Workspace carving (byte offsets).
 struct Layout {
-  size_t vt = 0, G = 0, B = 0, Sf = 0, Sb = 0, W = 0, pO = 0, pml = 0, q8 = 0, k8 = 0, amax = 0;
+  size_t vt = 0, vtx = 0, G = 0, B = 0, Sf = 0, Sb = 0, W = 0, pO = 0, pml = 0, q8 = 0, k8 = 0, amax = 0;
   size_t total = 0;
 };
 
-Layout layout(int F, int N, int H, int d, int prec) {
+// T: extra tokens after the F*N video tokens (0: none)
+Layout layout(int F, int N, int H, int d, int prec, int T = 0) {
   Layout L;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -76,16 +85,19 @@ Layout layout(int F, int N, int H, int d, int prec) {
   vdn::attn_split_plan(F, &nsplit, &fs);
   const size_t na = F >= 2 ? 2 : 1;
   L.vt = take(prec == VDN_PREC_FP32 ? 0 : static_cast<size_t>(H) * F * nb * d * 64 * 2);
+  L.vtx = take(static_cast<size_t>(H) * ((static_cast<size_t>(T) + 63) / 64) * d * 64 * 2);
   L.G = take(static_cast<size_t>(F) * H * dd * 4);
   L.B = take(static_cast<size_t>(F) * H * dd * 4);
   L.Sf = take(C * H * dd * 4);
   L.Sb = take(C * H * dd * 4);
   L.W = take(C * H * dd * 4);              // bf16 (first half), or fp32
-  L.pO = take(static_cast<size_t>(nsplit) * H * na * N * d * 4);
-  L.pml = take(static_cast<size_t>(nsplit) * H * na * N * 2 * 4);
+  const size_t rows = na * N + static_cast<size_t>(T);      // split rows per head: anchors, extras
+  L.pO = take(static_cast<size_t>(nsplit) * H * rows * d * 4);
+  L.pml = take(static_cast<size_t>(nsplit) * H * rows * 2 * 4);
   if (prec == VDN_PREC_BF16_FP8QK) {
-    L.q8 = take(static_cast<size_t>(F) * N * H * d);
-    L.k8 = take(static_cast<size_t>(F) * N * H * d);
+    const size_t ntok = static_cast<size_t>(F) * N + T;
+    L.q8 = take(ntok * H * d);
+    L.k8 = take(ntok * H * d);
     L.amax = take(2 * static_cast<size_t>(H) * 4);
   }
   L.total = off;
@@ -98,8 +110,8 @@ struct WsPtr {
   T* at(size_t off) const { return reinterpret_cast<T*>(base + off); }
 };
 
-int check_ws(int F, int N, int H, int d, int prec, void* ws, size_t ws_bytes, Layout* L) {
-  *L = layout(F, N, H, d, prec);
+int check_ws(int F, int N, int H, int d, int prec, void* ws, size_t ws_bytes, Layout* L, int T = 0) {
+  *L = layout(F, N, H, d, prec, T);
   if (ws == nullptr && L->total > 0) return VDN_ERR_INVALID_ARG;
   if (!aligned(ws, 256)) return VDN_ERR_INVALID_ARG;
   if (ws_bytes < L->total) return VDN_ERR_WORKSPACE;
@@ -110,17 +122,22 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 // ---- pieces of the launch sequence
 // W: bf16 readout weights to fold into the attention epilogue (O = O_soft + W q on
-// the non-anchor frames), or null for O = O_soft
+// the non-anchor frames), or null for O = O_soft.  T: extra tokens after the video
+// tokens of q, k, v, O (0: none).
 int run_softmax(const void* q, const void* k, const void* v, int F, int N, int H, int d, int prec,
-                void* O, const Layout& L, WsPtr ws, bool vt_ready, const uint16_t* W, hipStream_t st) {
+                void* O, const Layout& L, WsPtr ws, bool vt_ready, const uint16_t* W, hipStream_t st,
+                int T = 0) {
   const uint8_t* q8 = nullptr;
   const uint8_t* k8 = nullptr;
   const float* amax = nullptr;
   if (prec == VDN_PREC_BF16_FP8QK) {
+    // per-head scales over every token of the layer (the quantiser sees F*N+T
+    // tokens as one frame)
+    const int qF = T > 0 ? 1 : F, qN = T > 0 ? F * N + T : N;
     VDN_TRY(mark(VDN_STAGE_QUANT, 0, st));
-    VDN_TRY(vdn::launch_fp8_quant(static_cast<const uint16_t*>(q), F, N, H, d, ws.at<uint8_t>(L.q8),
+    VDN_TRY(vdn::launch_fp8_quant(static_cast<const uint16_t*>(q), qF, qN, H, d, ws.at<uint8_t>(L.q8),
                                   ws.at<float>(L.amax), st));
-    VDN_TRY(vdn::launch_fp8_quant(static_cast<const uint16_t*>(k), F, N, H, d, ws.at<uint8_t>(L.k8),
+    VDN_TRY(vdn::launch_fp8_quant(static_cast<const uint16_t*>(k), qF, qN, H, d, ws.at<uint8_t>(L.k8),
                                   ws.at<float>(L.amax) + H, st));
     VDN_TRY(mark(VDN_STAGE_QUANT, 1, st));
     q8 = ws.at<uint8_t>(L.q8);
@@ -131,13 +148,20 @@ int run_softmax(const void* q, const void* k, const void* v, int F, int N, int H
     VDN_STAGE(VDN_STAGE_PREP, st,
               vdn::launch_prep(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), F, N, H,
                                d, ws.at<uint16_t>(L.vt), nullptr, nullptr, 0, st));
+  if (T > 0) {
+    // the extra tokens' V^T blocks, laid out as one more frame of T tokens (no
+    // Grams; a few microseconds, outside the stage brackets)
+    const size_t voff = static_cast<size_t>(F) * N * H * d;
+    VDN_TRY(vdn::launch_prep(static_cast<const uint16_t*>(k) + voff, static_cast<const uint16_t*>(v) + voff, 1, T,
+                             H, d, ws.at<uint16_t>(L.vtx), nullptr, nullptr, 0, st));
+  }
   const int kprec = prec == VDN_PREC_FP32 ? 0 : (prec == VDN_PREC_BF16 ? 1 : 2);
   VDN_STAGE(VDN_STAGE_ATTN, st,
             vdn::launch_attn(kprec, q, k, v, ws.at<uint16_t>(L.vt), q8, k8, amax, F, N, H, d, O,
-                             ws.at<float>(L.pO), ws.at<float>(L.pml), W, st));
+                             ws.at<float>(L.pO), ws.at<float>(L.pml), W, T, ws.at<uint16_t>(L.vtx), st));
   VDN_STAGE(VDN_STAGE_COMBINE, st,
             vdn::launch_combine(prec == VDN_PREC_FP32 ? 0 : 1, ws.at<float>(L.pO), ws.at<float>(L.pml),
-                                F, N, H, d, O, st));
+                                F, N, T, H, d, O, st));
   return VDN_OK;
 }
 
@@ -254,6 +278,34 @@ int vdn_hybrid_attn(const void* q, const void* k, const void* v, const float* be
   if (!bf16)
     VDN_STAGE(VDN_STAGE_READOUT, st, vdn::launch_readout(0, q, ws.at<void>(L.W), F, N, H, d, O, 1, st));
   return VDN_OK;
+}
+
+size_t vdn_workspace_bytes_mixed(int F, int N, int T, int H, int d, int precision) {
+  if (check_shape(F, N, H, d, precision) != VDN_OK || check_extra(F, N, T, precision) != VDN_OK) return 0;
+  return layout(F, N, H, d, precision, T).total;
+}
+
+int vdn_hybrid_attn_mixed(const void* q, const void* k, const void* v, const float* beta, const float* gate,
+                          int F, int N, int T, int H, int d, int precision, void* O, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int s = check_shape(F, N, H, d, precision);
+  if (s != VDN_OK) return s;
+  if ((s = check_extra(F, N, T, precision)) != VDN_OK) return s;
+  if (T == 0)
+    return vdn_hybrid_attn(q, k, v, beta, gate, F, N, H, d, precision, O, workspace, workspace_bytes, stream);
+  if (!q || !k || !v || !beta || !gate || !O) return VDN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(O, 16)) return VDN_ERR_INVALID_ARG;
+  Layout L;
+  if ((s = check_ws(F, N, H, d, precision, workspace, workspace_bytes, &L, T)) != VDN_OK) return s;
+  const hipStream_t st = as_stream(stream);
+  WsPtr ws{static_cast<unsigned char*>(workspace)};
+  float* Sf = ws.at<float>(L.Sf);
+  float* Sb = ws.at<float>(L.Sb);
+  // the linear branch sees the video tokens only (the first F*N of every tensor)
+  if ((s = run_states(k, v, beta, F, N, H, d, precision, Sf, Sb, L, ws, st)) != VDN_OK) return s;
+  VDN_STAGE(VDN_STAGE_WPREP, st,
+            vdn::launch_wprep(Sf, Sb, gate, vdn::num_chunks(F), H, d, 1, ws.at<void>(L.W), st));
+  return run_softmax(q, k, v, F, N, H, d, precision, O, L, ws, true, ws.at<uint16_t>(L.W), st, T);
 }
 
 int vdn_softmax_branch(const void* q, const void* k, const void* v, int F, int N, int H, int d,

@@ -188,6 +188,12 @@ struct AttnArgs {
   int tiles_per_head;     // sum over chunks of the chunk items' tile counts
   int bq;                 // query rows per work item (32 per wave)
   float scale_log2;       // log2(e) / sqrt(D)
+  // extra (text / audio) tokens: T tokens after the F*N video tokens of q, k, v, O;
+  // every interaction involving one of them is plain softmax.  bf16 / fp8 paths.
+  int T;                  // 0: none
+  int nbx;                // 64-key blocks of the extra tokens
+  int qt_x;               // query tiles of the extra tokens' rows
+  const uint16_t* vtx;    // their V^T blocks [H][nbx][D][64], laid out as vt
 };
 
 constexpr int BQ = 128;   // queries per work item of attn_kernel (4 waves x 32)
@@ -695,6 +701,65 @@ __device__ inline Item decode_item(const AttnArgs& a) {
   return it;
 }
 
+// Work item when the layer has extra tokens.  Per head, per key split: the anchor
+// frames' query tiles, then the extra tokens' query tiles (anchor_idx = na); then
+// the chunk items as in decode_item.  The key list of a chunk item, and of the last
+// split of a split item, ends with the extra tokens: their slot is returned in
+// *xslot (-1 if none), after the it.nslots video frames.
+__device__ inline Item decode_item_x(const AttnArgs& a, int* xslot) {
+  Item it;
+  const int F = a.F, N = a.N;
+  const int G = a.na * a.qt_anchor + a.qt_x;             // split-item query tiles per split
+  const int na_h = G * a.nsplit;                         // split items per head
+  const int M = na_h + a.tiles_per_head;                 // items per head
+  const int b = blockIdx.x;
+  const int hh = b / M, p = b - hh * M;
+  const int q8 = M >> 3, m8 = M & 7, r = p & 7;
+  const int li = r * q8 + min(r, m8) + (p >> 3);         // item of head hh (XCD-contiguous)
+  it.wf = it.we = it.k_f0 = 0;
+  it.h = hh;
+  if (li < na_h) {
+    it.split = li / G;
+    const int g = li - it.split * G;
+    if (g < a.na * a.qt_anchor) {
+      it.anchor_idx = g / a.qt_anchor;
+      const int qt = g - it.anchor_idx * a.qt_anchor;
+      it.q_tok0 = (it.anchor_idx == 0 ? 0 : F - 1) * N + qt * a.bq;
+      it.q_rows = min(a.bq, N - qt * a.bq);
+    } else {
+      it.anchor_idx = a.na;
+      const int qt = g - a.na * a.qt_anchor;
+      it.q_tok0 = F * N + qt * a.bq;
+      it.q_rows = min(a.bq, a.T - qt * a.bq);
+    }
+    it.mode = 0;
+    it.k_f0 = it.split * a.fs;
+    it.nslots = min(F, it.k_f0 + a.fs) - it.k_f0;
+    *xslot = it.split == a.nsplit - 1 ? it.nslots : -1;
+  } else {
+    int rr = li - na_h;
+    it.split = -1;
+    it.anchor_idx = 0;
+    const int C = num_chunks(F);
+    int c = 0;
+    for (; c < C; ++c) {
+      const int nf = nq_end(c, F) - nq_first(c);
+      const int t = nf > 0 ? (nf * N + a.bq - 1) / a.bq : 0;
+      if (rr < t) break;
+      rr -= t;
+    }
+    const int tok_begin = nq_first(c) * N, tok_end = nq_end(c, F) * N;
+    it.q_tok0 = tok_begin + rr * a.bq;
+    it.q_rows = min(a.bq, tok_end - it.q_tok0);
+    it.mode = 1;
+    it.wf = win_first(c);
+    it.we = win_end(c, F);
+    it.nslots = (it.wf > 0 ? 1 : 0) + (it.we - it.wf) + (it.we < F ? 1 : 0);
+    *xslot = it.nslots;
+  }
+  return it;
+}
+
 // An item with every field read from the first lane: it is the same in every
 // lane, and this lets the compiler keep it and what derives from it in SGPRs.
 __device__ inline Item uniform_item(Item it) {
@@ -711,7 +776,7 @@ __device__ inline Item uniform_item(Item it) {
   return it;
 }
 
-template <int D, int PREC, int NW>
+template <int D, int PREC, int NW, bool XT>
 // (waves per SIMD: 2 at d = 128, which needs ~240 registers; the fp8 path at d = 64
 // fits 128 registers, i.e. two workgroups per CU)
 __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_lds_kernel(AttnArgs a) {
@@ -726,13 +791,18 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
   const size_t rs = (size_t)H * D;                 // token stride in elements
   const int nb = (N + BK - 1) / BK;
   // the item is wave-uniform; say so, so that tile bookkeeping stays in SGPRs
-  const Item it = uniform_item(decode_item(a));
+  int xs = -1;                 // with extra tokens: their slot in the key list
+  Item it0;
+  if constexpr (XT) it0 = decode_item_x(a, &xs);
+  else it0 = decode_item(a);
+  const Item it = uniform_item(it0);
+  const int xslot = XT ? __builtin_amdgcn_readfirstlane(xs) : -1;
   // the second wave of every SIMD issues first when both are ready: a fixed order
   // for the two waves that share the matrix core (measured 0.5-1 % faster than
   // the hardware's default arbitration; the reverse order gains the same)
   if (w >= NW / 2) __builtin_amdgcn_s_setprio(1);
   const int h = it.h;
-  const int ntiles = it.nslots * nb;
+  const int ntiles = it.nslots * nb + (XT && xslot >= 0 ? a.nbx : 0);
 
   // ---- Q operand fragments, resident for the whole item
   const int qi = 32 * w + j;
@@ -803,7 +873,7 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
   constexpr int LPT = KX + VX;
   auto issue_range = [&](int stage, int f, int b, int x0, int x1) {
     unsigned char* sbase = smem + stage * Cfg::STAGE;
-    const int nvalid = min(BK, N - BK * b);
+    const int nvalid = min(BK, (XT && f == F ? a.T : N) - BK * b);
     // buffer loads to LDS (MUBUF): unlike the FLAT-encoded global_load_lds they
     // leave the compiler free to wait for LDS reads one by one (lgkmcnt(n))
     const unsigned char* kt = kbase + (((size_t)f * N + BK * b) * rs + (size_t)h * D) * (FP8 ? 1 : 2);
@@ -817,7 +887,8 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_ptr)(sbase + 1024 * (x * NW + w)), 16, koff[x], 0, 0, 0);
     }
     const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(
-        a.vt + (((size_t)h * F + f) * nb + b) * (size_t)(D * BK));
+        XT && f == F ? a.vtx + ((size_t)h * a.nbx + b) * (size_t)(D * BK)
+                     : a.vt + (((size_t)h * F + f) * nb + b) * (size_t)(D * BK));
     const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vsrc, (uint32_t)(D * BK * 2));
 #pragma unroll
     for (int x = 0; x < VX; ++x) {
@@ -849,11 +920,19 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
   float m_run = FP8 ? -INFINITY : 0.f, l_run = 0.f;
   floatx16 nm = floatx16{};      // -m in every element: the first Q.K^T accumulator input
 
+  // with extra tokens, tiles t >= t_x (the last ones of the key list, when the
+  // item has them) are the extra tokens' 64-key blocks t - t_x, frame index F;
+  // the frame cursor above walks the video frames only
+  const int t_x = it.nslots * nb;
 #pragma unroll
   for (int x = 0; x < AHEAD; ++x) {
     if (x < ntiles) {
-      issue_range(x, ld_f, ld_b, 0, LPT);
-      next_load();
+      if (XT && x >= t_x) {
+        issue_range(x, F, x - t_x, 0, LPT);
+      } else {
+        issue_range(x, ld_f, ld_b, 0, LPT);
+        next_load();
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -863,10 +942,26 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
   for (int t = 0; t < ntiles; ++t) {
     const int stage = t & (NSTG - 1);
     const bool ld = t + AHEAD < ntiles;      // load tile t + AHEAD during this tile
-    const int ldf = ld_f, ldb = ld_b;
-    if (ld) next_load();
-    const int nvalid = min(BK, N - BK * b);
-    if (++b == nb) b = 0;
+    int ldf = ld_f, ldb = ld_b;
+    int nvalid;
+    if constexpr (XT) {
+      if (t + AHEAD >= t_x) {
+        ldf = F;
+        ldb = t + AHEAD - t_x;
+      } else if (ld) {
+        next_load();
+      }
+      if (t >= t_x) {
+        nvalid = min(BK, a.T - BK * (t - t_x));
+      } else {
+        nvalid = min(BK, N - BK * b);
+        if (++b == nb) b = 0;
+      }
+    } else {
+      if (ld) next_load();
+      nvalid = min(BK, N - BK * b);
+      if (++b == nb) b = 0;
+    }
     const unsigned char* sbase = smem + stage * Cfg::STAGE;
 
     // ---- S^T = K Q^T.  Operand fragments come from LDS in batches, double
@@ -1089,8 +1184,18 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(kargs->O) + ooff + dd) = pk;
       }
   } else {
-    const int n = it.q_tok0 - (it.anchor_idx == 0 ? 0 : (F - 1) * N) + qi;
-    const size_t row = (((size_t)it.split * H + h) * kargs->na + it.anchor_idx) * N + n;
+    size_t row;
+    if constexpr (XT) {
+      // rows per head: the anchor frames' N each, then the T extra tokens
+      const int na = kargs->na, R = na * N + kargs->T;
+      const int rr = it.anchor_idx < na
+                         ? it.anchor_idx * N + it.q_tok0 - (it.anchor_idx == 0 ? 0 : (F - 1) * N) + qi
+                         : na * N + it.q_tok0 - F * N + qi;
+      row = ((size_t)it.split * H + h) * R + rr;
+    } else {
+      const int n = it.q_tok0 - (it.anchor_idx == 0 ? 0 : (F - 1) * N) + qi;
+      row = (((size_t)it.split * H + h) * kargs->na + it.anchor_idx) * N + n;
+    }
     float* po = kargs->part_O + row * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -1108,19 +1213,19 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
 }
 
 // ============================================================ combine
-// One thread per (split-merged row, 4 channels).  Rows: [H][na][N].
+// One thread per (split-merged row, 4 channels).  Rows: [H][na * N + T], the
+// anchor frames' tokens, then the extra tokens'.
 template <int D, bool F32OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_O,
                                                       const float* __restrict__ part_ml, int F,
-                                                      int N, int H, int na, int nsplit, void* O) {
-  const size_t rows = (size_t)H * na * N;
+                                                      int N, int T, int H, int na, int nsplit, void* O) {
+  const int R = na * N + T;
+  const size_t rows = (size_t)H * R;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= rows * (D / 4)) return;
   const size_t row = idx / (D / 4);
   const int c4 = idx % (D / 4);
-  const int n = row % N;
-  const int ai = (row / N) % na;
-  const int h = row / ((size_t)N * na);
+  const int h = row / R, rr = row % R;
   float m = -INFINITY;
   for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_ml[2 * (s * rows + row)]);
   float l = 0.f;
@@ -1136,8 +1241,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     acc.w += wgt * x.w;
   }
   const float inv = 1.f / l;
-  const int qf = ai == 0 ? 0 : F - 1;
-  const size_t off = ((size_t)qf * N + n) * H * D + (size_t)h * D + 4 * c4;
+  const size_t tok = rr < na * N ? (size_t)(rr < N ? 0 : F - 1) * N + rr % N : (size_t)F * N + (rr - na * N);
+  const size_t off = tok * H * D + (size_t)h * D + 4 * c4;
   if constexpr (F32OUT) {
     *reinterpret_cast<float4*>(static_cast<float*>(O) + off) =
         make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
@@ -1257,7 +1362,8 @@ void attn_split_plan(int F, int* nsplit, int* fs) {
 // work-item counts for query tiles of a.bq rows
 static void attn_items(AttnArgs& a) {
   a.qt_anchor = (a.N + a.bq - 1) / a.bq;
-  a.n_anchor_items = a.H * a.na * a.qt_anchor * a.nsplit;
+  a.qt_x = (a.T + a.bq - 1) / a.bq;
+  a.n_anchor_items = a.H * (a.na * a.qt_anchor + a.qt_x) * a.nsplit;
   int tph = 0;
   for (int c = 0; c < num_chunks(a.F); ++c) {
     const int nf = nq_end(c, a.F) - nq_first(c);
@@ -1291,20 +1397,30 @@ static hipError_t attn_f32(const AttnArgs& a, hipStream_t st) {
 }
 template <int D, int PREC>
 static hipError_t attn_lds(const AttnArgs& a, hipStream_t st) {
+  if (a.T > 0) {
+    static bool done_x = false;
+    return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, true>, kLdsStages * LdsCfg<D, PREC>::STAGE, &done_x,
+                       a, st, 64 * kLdsWaves);
+  }
   static bool done = false;
-  return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves>, kLdsStages * LdsCfg<D, PREC>::STAGE, &done, a, st,
-                     64 * kLdsWaves);
+  return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false>, kLdsStages * LdsCfg<D, PREC>::STAGE, &done, a,
+                     st, 64 * kLdsWaves);
 }
 
 hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, const uint16_t* vt,
                        const uint8_t* q8, const uint8_t* k8, const float* amax, int F, int N, int H,
                        int D, void* O, float* part_O, float* part_ml, const uint16_t* W,
-                       hipStream_t st) {
+                       int T, const uint16_t* vtx, hipStream_t st) {
   AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.vt = vt; a.q8 = q8; a.k8 = k8; a.amax = amax;
   a.O = O; a.part_O = part_O; a.part_ml = part_ml;
   a.W = W;
-  if (prec == 0 && W != nullptr) return hipErrorInvalidValue;   // the fp32 kernel has no fused readout
+  a.T = T;
+  a.nbx = (T + BK - 1) / BK;
+  a.vtx = vtx;
+  // the fp32 kernel has neither the fused readout nor extra tokens
+  if (prec == 0 && (W != nullptr || T != 0)) return hipErrorInvalidValue;
+  if (T < 0 || (T > 0 && vtx == nullptr)) return hipErrorInvalidValue;
   a.F = F; a.N = N; a.H = H;
   attn_split_plan(F, &a.nsplit, &a.fs);
   a.na = F >= 2 ? 2 : 1;
@@ -1324,21 +1440,21 @@ hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, co
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_combine(int prec, const float* part_O, const float* part_ml, int F, int N, int H,
-                          int D, void* O, hipStream_t st) {
+hipError_t launch_combine(int prec, const float* part_O, const float* part_ml, int F, int N, int T,
+                          int H, int D, void* O, hipStream_t st) {
   int nsplit, fs;
   attn_split_plan(F, &nsplit, &fs);
   const int na = F >= 2 ? 2 : 1;
-  const size_t threads = (size_t)H * na * N * (D / 4);
+  const size_t threads = (size_t)H * ((size_t)na * N + T) * (D / 4);
   const dim3 grid((unsigned)((threads + 255) / 256));
 #define VDN_COMB(DD)                                                                                   \
   if (D == DD) {                                                                                       \
     if (prec == 0)                                                                                     \
-      hipLaunchKernelGGL((combine_kernel<DD, true>), grid, dim3(256), 0, st, part_O, part_ml, F, N, H, \
-                         na, nsplit, O);                                                               \
+      hipLaunchKernelGGL((combine_kernel<DD, true>), grid, dim3(256), 0, st, part_O, part_ml, F, N, T, \
+                         H, na, nsplit, O);                                                            \
     else                                                                                               \
       hipLaunchKernelGGL((combine_kernel<DD, false>), grid, dim3(256), 0, st, part_O, part_ml, F, N,   \
-                         H, na, nsplit, O);                                                            \
+                         T, H, na, nsplit, O);                                                         \
     return hipGetLastError();                                                                          \
   }
   VDN_COMB(32) VDN_COMB(64) VDN_COMB(128)

@@ -83,6 +83,25 @@ int vdn_hybrid_attn(const void* q, const void* k, const void* v,
                     int F, int N, int H, int d, int precision,
                     void* O, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The layer with T extra (text or audio) tokens in the same sequence (arXiv
+ * abstract page, Abstract; ananclaw note "Video DeltaNet ... critical read",
+ * section 一、方法拆解: the hybrid covers video-to-video interactions only, every
+ * interaction that involves a text or audio token stays plain softmax).
+ * q, k, v, O: [F*N + T, H, d], the F*N video tokens (frame-major, as in
+ * vdn_hybrid_attn) followed by the T extra tokens; beta: [F, H]; gate: [H, d].
+ *   - a video query's softmax covers its key frames and all T extra tokens, in one
+ *     normalisation; its linear output and merge are as in vdn_hybrid_attn;
+ *   - an extra token's output is softmax attention over all F*N + T tokens;
+ *   - the states see the video tokens only.
+ * T = 0 is vdn_hybrid_attn.  T > 0 needs VDN_PREC_BF16 or VDN_PREC_BF16_FP8QK
+ * (else VDN_ERR_UNSUPPORTED; the fp8 per-head scales then cover all F*N + T
+ * tokens) and a workspace of vdn_workspace_bytes_mixed bytes. */
+size_t vdn_workspace_bytes_mixed(int F, int N, int T, int H, int d, int precision);
+int vdn_hybrid_attn_mixed(const void* q, const void* k, const void* v,
+                          const float* beta, const float* gate,
+                          int F, int N, int T, int H, int d, int precision,
+                          void* O, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Softmax branch alone (part (a)): O_soft[i, n, h] = sum over tokens (j, m) of
  * the key frames of query frame i of softmax_{(j,m)}(q_{i,n,h} . k_{j,m,h} / sqrt(d))
  * v_{j,m,h}, with the window + anchor frame sets of the sd114.wiki article,
