@@ -27,7 +27,9 @@ It computes, in float64 with NumPy, exactly what the layer is defined to compute
     Hybrid Attention Architecture: outputs merged by a gating mechanism];
   * with extra (text / audio) tokens in the layer, plain softmax for every
     interaction that involves one of them [arXiv abstract; ananclaw note,
-    section 一、方法拆解].
+    section 一、方法拆解];
+  * separate output projections of the two branches, the gate on the linear
+    branch [same abstract and note section].
 
 Tensor layout: q, k, v are [F, N, H, d] (frame, token-in-frame, head, channel);
 beta is [F, H]; gate is [H, d]; states are [C, H, d, d] with C = ceil(F / 5),
@@ -267,6 +269,34 @@ def hybrid(q, k, v, beta, gate, dense=False):
     S_fwd, S_bwd = vda_states(k, v, beta)
     O_lin = linear_branch(q, S_fwd, S_bwd)
     return merge(O_soft, O_lin, gate), O_soft, O_lin
+
+
+# --------------------------------------------------------------------------
+# Separate output projections of the two branches
+# --------------------------------------------------------------------------
+# Each branch has its own output projection, and learnable gates set the linear
+# branch's share [arXiv abstract page, Abstract; ananclaw note, section 一、方法拆解].
+# With W_s, W_l in R^{D x H*d} (per token, the H*d head outputs flattened head-major)
+# and the per-(head, channel) gate g of the merge:
+#     Y = O_soft W_s^T + (g * O_lin) W_l^T.
+# W_s = W_l = W gives merge(O_soft, O_lin, g) W^T.
+
+def output_projection(O_soft, O_lin, gate, W_s, W_l) -> np.ndarray:
+    """Y [F, N, D] from O_soft, O_lin [F, N, H, d], gate [H, d], W_s, W_l [D, H*d]."""
+    O_soft = np.asarray(O_soft, np.float64)
+    F, N, H, d = O_soft.shape
+    lin = np.asarray(gate, np.float64)[None, None] * np.asarray(O_lin, np.float64)
+    Ws = np.asarray(W_s, np.float64)
+    Wl = np.asarray(W_l, np.float64)
+    return O_soft.reshape(F, N, H * d) @ Ws.T + lin.reshape(F, N, H * d) @ Wl.T
+
+
+def hybrid_proj(q, k, v, beta, gate, W_s, W_l):
+    """The layer followed by the two output projections.  Returns (Y, O_soft, O_lin)."""
+    O_soft = softmax_branch(q, k, v)
+    S_fwd, S_bwd = vda_states(k, v, beta)
+    O_lin = linear_branch(q, S_fwd, S_bwd)
+    return output_projection(O_soft, O_lin, gate, W_s, W_l), O_soft, O_lin
 
 
 # --------------------------------------------------------------------------

@@ -209,6 +209,37 @@ def test_mixed_layer_linear_branch_is_video_only():
     assert Oxe.shape == (0, H, d)
 
 
+# ---------------------------------------------------------------- output projections
+
+def test_projection_special_weights():
+    # identity and zero weights reduce the projection to each branch alone, shared
+    # weights to the merged layer followed by one projection, and the result is
+    # linear in each weight matrix
+    F, N, H, d = 22, 3, 2, 8
+    Hd = H * d
+    q, k, v = small_inputs(F, N, H, d, seed=6)
+    beta, gate = vdn_synth.beta(F, H, seed=6), vdn_synth.gate(H, d, seed=6)
+    O, Os, Ol = orc.hybrid(q, k, v, beta, gate)
+    I, Z = np.eye(Hd), np.zeros((Hd, Hd))
+    Y, Ys, Yl = orc.hybrid_proj(q, k, v, beta, gate, I, Z)
+    np.testing.assert_allclose(Y, Os.reshape(F, N, Hd), rtol=1e-12, atol=1e-14)
+    Y, _, _ = orc.hybrid_proj(q, k, v, beta, gate, Z, I)
+    np.testing.assert_allclose(Y, (gate[None, None] * Ol).reshape(F, N, Hd), rtol=1e-12, atol=1e-14)
+    Wp = vdn_synth.proj_weights(5, Hd, seed=6).astype(np.float64)
+    W1, W2 = Wp[:, :Hd], Wp[:, Hd:]
+    Y, _, _ = orc.hybrid_proj(q, k, v, beta, gate, W1, W1)
+    np.testing.assert_allclose(Y, O.reshape(F, N, Hd) @ W1.T, rtol=1e-11, atol=1e-12)
+    Ya, _, _ = orc.hybrid_proj(q, k, v, beta, gate, W1, W2)
+    Yb, _, _ = orc.hybrid_proj(q, k, v, beta, gate, W1 + W2, W2)
+    Yc, _, _ = orc.hybrid_proj(q, k, v, beta, gate, W2, np.zeros_like(W2))
+    np.testing.assert_allclose(Yb, Ya + Yc, rtol=1e-10, atol=1e-12)
+    # one output channel by hand: a plain sum over heads and channels
+    t_f, t_n, c = 13, 1, 3
+    ref = sum(Os[t_f, t_n, h, e] * W1[c, h * d + e] + gate[h, e] * Ol[t_f, t_n, h, e] * W2[c, h * d + e]
+              for h in range(H) for e in range(d))
+    assert abs(Ya[t_f, t_n, c] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
 # ---------------------------------------------------------------- VDA update
 
 def test_update_is_least_squares_minimiser():

@@ -15,7 +15,8 @@ Recipe (every configuration):
     attention logits at standard deviation ~4);
   * extra (text / audio) tokens, when a layer has them: q, k, v of T tokens, the
     same distributions, one T x d block per (tensor, head) from
-    SeedSequence([seed, 5 + tensor_id, head]), laid out [T, H, d].
+    SeedSequence([seed, 5 + tensor_id, head]), laid out [T, H, d];
+  * output projection weights [W_s | W_l], N(0, 1/(H*d)), from SeedSequence([seed, 8]).
 
 Block seeding lets a test regenerate only the frames and heads it samples.
 Tensors are laid out [F, N, H, d] (token-major, one token = H*d contiguous values).
@@ -67,6 +68,12 @@ def extra(name: str, T: int, H: int, d: int, seed: int = 0, q_std: float = 1.0) 
             x = x * np.float32(q_std)
         out[:, h, :] = x
     return out
+
+
+def proj_weights(D: int, Hd: int, seed: int = 0) -> np.ndarray:
+    """Output projections of the two branches side by side, [W_s | W_l]: float32
+    [D, 2*Hd], N(0, 1/Hd) entries from SeedSequence([seed, 8])."""
+    return (_rng(seed, 8).standard_normal((D, 2 * Hd), dtype=np.float32) / np.float32(np.sqrt(Hd))).astype(np.float32)
 
 
 def beta(F: int, H: int, seed: int = 0) -> np.ndarray:
