@@ -226,7 +226,7 @@ def main():
     # stages the layer runs in this precision: the quantiser only with fp8 q.k; the
     # bf16 and fp8 layers run the readout and merge in the attention kernel
     run = [st for st, name in enumerate(vdn.STAGES)
-           if (name != "quant" or prec == "bf16_fp8qk") and name != "readout"]
+           if (name != "quant" or prec == "bf16_fp8qk") and name not in ("readout", "proj")]
     ev = {(s, st): (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for s in range(args.steps) for st in run}
     for pair in ev.values():       # torch creates the HIP event on its first record

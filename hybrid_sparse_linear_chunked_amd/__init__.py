@@ -21,7 +21,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 PREC_FP32, PREC_BF16, PREC_BF16_FP8QK = 0, 1, 2
 PRECISIONS = {"fp32": PREC_FP32, "bf16": PREC_BF16, "bf16_fp8qk": PREC_BF16_FP8QK}
 SCHED_COLS = 13
-STAGES = ("prep", "factor", "scan", "wprep", "attn", "combine", "readout", "quant")
+STAGES = ("prep", "factor", "scan", "wprep", "attn", "combine", "readout", "quant", "proj")
 
 # C signatures: (name, restype, argtypes)
 _P = ctypes.c_void_p
@@ -31,6 +31,9 @@ _SIGS = {
     "vdn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "vdn_hybrid_attn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "vdn_workspace_bytes_mixed": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "vdn_workspace_bytes_proj": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "vdn_hybrid_attn_proj": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "vdn_out_proj": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "vdn_hybrid_attn_mixed": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "vdn_softmax_branch": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "vdn_vda_states": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
@@ -207,6 +210,51 @@ def hybrid_attn_mixed(q, k, v, beta, gate, F, N, precision=None, out=None, works
                                       workspace.data_ptr(), workspace.numel(), _stream())
     _check(st, "vdn_hybrid_attn_mixed")
     return O
+
+
+def new_workspace_proj(F, N, H, d, D, precision, device="cuda"):
+    """A workspace tensor for repeated hybrid_attn_proj calls with this shape."""
+    prec = precision if isinstance(precision, int) else PRECISIONS[precision]
+    need = int(load().vdn_workspace_bytes_proj(F, N, H, d, D, prec))
+    if need == 0:
+        raise VdnError(ERR_UNSUPPORTED, "vdn_workspace_bytes_proj")
+    return _torch().empty(need, dtype=_torch().uint8, device=device)
+
+
+def hybrid_attn_proj(q, k, v, beta, gate, Wp, precision=None, out=None, workspace=None):
+    """Y = O_soft W_s^T + (g (.) O_lin) W_l^T: q, k, v bf16 [F, N, H, d]; Wp bf16
+    [D, 2*H*d] = [W_s | W_l].  Returns Y bf16 [F*N, D]."""
+    torch = _torch()
+    prec = _precision_of(q, precision)
+    F, N, H, d = q.shape
+    D = Wp.shape[0]
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_io(name, x, torch.bfloat16, (F, N, H, d))
+    _check_io("beta", beta, torch.float32, (F, H))
+    _check_io("gate", gate, torch.float32, (H, d))
+    _check_io("Wp", Wp, torch.bfloat16, (D, 2 * H * d))
+    Y = torch.empty((F * N, D), dtype=torch.bfloat16, device=q.device) if out is None else out
+    _check_io("out", Y, torch.bfloat16, (F * N, D))
+    if workspace is None:
+        workspace = new_workspace_proj(F, N, H, d, D, prec, device=q.device)
+    st = load().vdn_hybrid_attn_proj(q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(), gate.data_ptr(),
+                                     Wp.data_ptr(), F, N, H, d, D, prec, Y.data_ptr(), workspace.data_ptr(),
+                                     workspace.numel(), _stream())
+    _check(st, "vdn_hybrid_attn_proj")
+    return Y
+
+
+def out_proj(A, B, out=None):
+    """Y[M, N] = A[M, K] B[N, K]^T in bf16 (fp32 accumulation)."""
+    torch = _torch()
+    M, K = A.shape
+    N = B.shape[0]
+    _check_io("A", A, torch.bfloat16, (M, K))
+    _check_io("B", B, torch.bfloat16, (N, K))
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device) if out is None else out
+    _check_io("out", Y, torch.bfloat16, (M, N))
+    _check(load().vdn_out_proj(A.data_ptr(), B.data_ptr(), M, K, N, Y.data_ptr(), _stream()), "vdn_out_proj")
+    return Y
 
 
 def softmax_branch(q, k, v, precision=None, out=None, workspace=None):

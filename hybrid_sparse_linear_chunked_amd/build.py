@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libvdn_hybrid_attn.so")
-SOURCES = ["api.cpp", "attn.hip", "vda.hip"]
+SOURCES = ["api.cpp", "attn.hip", "vda.hip", "proj.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -123,10 +123,11 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 // ---- pieces of the launch sequence
 // W: bf16 readout weights to fold into the attention epilogue (O = O_soft + W q on
 // the non-anchor frames), or null for O = O_soft.  T: extra tokens after the video
-// tokens of q, k, v, O (0: none).
+// tokens of q, k, v, O (0: none).  split: O is [F*N][2][H][d], O_soft then W q
+// (zero on the anchor frames), the output projection's input.
 int run_softmax(const void* q, const void* k, const void* v, int F, int N, int H, int d, int prec,
                 void* O, const Layout& L, WsPtr ws, bool vt_ready, const uint16_t* W, hipStream_t st,
-                int T = 0) {
+                int T = 0, int split = 0) {
   const uint8_t* q8 = nullptr;
   const uint8_t* k8 = nullptr;
   const float* amax = nullptr;
@@ -158,10 +159,10 @@ int run_softmax(const void* q, const void* k, const void* v, int F, int N, int H
   const int kprec = prec == VDN_PREC_FP32 ? 0 : (prec == VDN_PREC_BF16 ? 1 : 2);
   VDN_STAGE(VDN_STAGE_ATTN, st,
             vdn::launch_attn(kprec, q, k, v, ws.at<uint16_t>(L.vt), q8, k8, amax, F, N, H, d, O,
-                             ws.at<float>(L.pO), ws.at<float>(L.pml), W, T, ws.at<uint16_t>(L.vtx), st));
+                             ws.at<float>(L.pO), ws.at<float>(L.pml), W, T, ws.at<uint16_t>(L.vtx), split, st));
   VDN_STAGE(VDN_STAGE_COMBINE, st,
             vdn::launch_combine(prec == VDN_PREC_FP32 ? 0 : 1, ws.at<float>(L.pO), ws.at<float>(L.pml),
-                                F, N, T, H, d, O, st));
+                                F, N, T, H, d, O, split, st));
   return VDN_OK;
 }
 
@@ -277,6 +278,61 @@ int vdn_hybrid_attn(const void* q, const void* k, const void* v, const float* be
   if ((s = run_softmax(q, k, v, F, N, H, d, precision, O, L, ws, true, Wfused, st)) != VDN_OK) return s;
   if (!bf16)
     VDN_STAGE(VDN_STAGE_READOUT, st, vdn::launch_readout(0, q, ws.at<void>(L.W), F, N, H, d, O, 1, st));
+  return VDN_OK;
+}
+
+// ---- the layer followed by the two branches' output projections
+size_t layer_ws_proj(const Layout& L, int F, int N, int H, int d) {
+  return L.total + al256(static_cast<size_t>(F) * N * 2 * H * d * 2);   // [F*N][2][H][d] bf16
+}
+
+size_t vdn_workspace_bytes_proj(int F, int N, int H, int d, int D, int precision) {
+  if (check_shape(F, N, H, d, precision) != VDN_OK) return 0;
+  if (precision == VDN_PREC_FP32 || D < 8 || D % 8 != 0) return 0;
+  return layer_ws_proj(layout(F, N, H, d, precision), F, N, H, d);
+}
+
+int vdn_hybrid_attn_proj(const void* q, const void* k, const void* v, const float* beta, const float* gate,
+                         const void* Wp, int F, int N, int H, int d, int D, int precision, void* Y,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  int s = check_shape(F, N, H, d, precision);
+  if (s != VDN_OK) return s;
+  if (precision == VDN_PREC_FP32) return VDN_ERR_UNSUPPORTED;
+  if (D < 8 || D % 8 != 0) return VDN_ERR_UNSUPPORTED;
+  if (static_cast<long long>(256) * 2 * (2LL * H * d) >= (1LL << 32)) return VDN_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !beta || !gate || !Wp || !Y) return VDN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(Wp, 16) || !aligned(Y, 16))
+    return VDN_ERR_INVALID_ARG;
+  Layout L = layout(F, N, H, d, precision);
+  if (workspace == nullptr || !aligned(workspace, 256)) return VDN_ERR_INVALID_ARG;
+  if (workspace_bytes < layer_ws_proj(L, F, N, H, d)) return VDN_ERR_WORKSPACE;
+  const hipStream_t st = as_stream(stream);
+  WsPtr ws{static_cast<unsigned char*>(workspace)};
+  uint16_t* Acat = ws.at<uint16_t>(L.total);           // [F*N][2][H][d]: O_soft, g (.) O_lin
+  if ((s = run_states(k, v, beta, F, N, H, d, precision, ws.at<float>(L.Sf), ws.at<float>(L.Sb), L, ws, st)) !=
+      VDN_OK)
+    return s;
+  VDN_STAGE(VDN_STAGE_WPREP, st,
+            vdn::launch_wprep(ws.at<float>(L.Sf), ws.at<float>(L.Sb), gate, vdn::num_chunks(F), H, d, 1,
+                              ws.at<void>(L.W), st));
+  if ((s = run_softmax(q, k, v, F, N, H, d, precision, Acat, L, ws, true, ws.at<uint16_t>(L.W), st, 0, 1)) !=
+      VDN_OK)
+    return s;
+  VDN_STAGE(VDN_STAGE_PROJ, st,
+            vdn::launch_proj(Acat, static_cast<const uint16_t*>(Wp), F * N, D, 2 * H * d, static_cast<uint16_t*>(Y),
+                             st));
+  return VDN_OK;
+}
+
+int vdn_out_proj(const void* A, const void* B, int M, int K, int N, void* Y, void* stream) {
+  if (!A || !B || !Y) return VDN_ERR_INVALID_ARG;
+  if (M < 1 || K < 1 || N < 1) return VDN_ERR_INVALID_ARG;
+  if (K % 64 != 0 || N % 8 != 0 || static_cast<long long>(256) * 2 * K >= (1LL << 32)) return VDN_ERR_UNSUPPORTED;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(Y, 16)) return VDN_ERR_INVALID_ARG;
+  const hipStream_t st = as_stream(stream);
+  VDN_STAGE(VDN_STAGE_PROJ, st,
+            vdn::launch_proj(static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), M, N, K,
+                             static_cast<uint16_t*>(Y), st));
   return VDN_OK;
 }
 

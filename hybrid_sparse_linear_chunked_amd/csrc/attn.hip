@@ -776,7 +776,10 @@ __device__ inline Item uniform_item(Item it) {
   return it;
 }
 
-template <int D, int PREC, int NW, bool XT>
+// XT: the layer has extra tokens.  SPLIT: chunk items write O_soft and g (.) O_lin
+// side by side (token stride 2 H D, the output projection's input) instead of
+// their sum.
+template <int D, int PREC, int NW, bool XT, bool SPLIT>
 // (waves per SIMD: 2 at d = 128, which needs ~240 registers; the fp8 path at d = 64
 // fits 128 registers, i.e. two workgroups per CU)
 __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_lds_kernel(AttnArgs a) {
@@ -1143,6 +1146,47 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
   // (all lanes take part in the MFMAs: lane j also supplies row j of W; rows of
   // Q past the item's end are zeros)
   float inv = 1.f / l_tot;
+  if constexpr (SPLIT) {
+    if (lin) {
+      constexpr int QS = D / 16;
+      bf16x8 qr[QS];
+      float us;
+      if constexpr (FP8) {
+        const uint16_t* q = static_cast<const uint16_t*>(a.q);
+#pragma unroll
+        for (int s = 0; s < QS; ++s)
+          qr[s] = qvalid ? *reinterpret_cast<const bf16x8*>(q + qoff + 16 * s + 8 * hf) : bf16x8{};
+        us = 1.f;
+      } else {
+#pragma unroll
+        for (int s = 0; s < QS; ++s) qr[s] = qb[s];
+        us = 1.f / kargs->scale_log2;
+      }
+      // token stride 2 H D: O_soft at h D, g (.) O_lin at H D + h D
+      uint16_t* ao = static_cast<uint16_t*>(kargs->O) + (size_t)(it.q_tok0 + qi) * (2 * rs) + (size_t)h * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        floatx16 acc = floatx16{};
+#pragma unroll
+        for (int s = 0; s < QS; ++s)
+          acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(smem + (32 * db + j) * WP + 16 * (2 * s + hf)), qr[s], acc);
+        if (qvalid) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int dd = 32 * db + 8 * g + 4 * hf;
+            const floatx16& c = o[db];
+            *reinterpret_cast<uint2*>(ao + dd) =
+                make_uint2(pack_bf16x2(c[4 * g + 0] * inv, c[4 * g + 1] * inv),
+                           pack_bf16x2(c[4 * g + 2] * inv, c[4 * g + 3] * inv));
+            *reinterpret_cast<uint2*>(ao + rs + dd) =
+                make_uint2(pack_bf16x2(acc[4 * g + 0] * us, acc[4 * g + 1] * us),
+                           pack_bf16x2(acc[4 * g + 2] * us, acc[4 * g + 3] * us));
+          }
+        }
+      }
+      return;
+    }
+  }
   if (lin) {
     // Q in bf16 as the B operand: the bf16 path's resident fragments carry the
     // factor log2(e)/sqrt(d), taken back out of the product; the fp8 path reads q
@@ -1215,10 +1259,14 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
 // ============================================================ combine
 // One thread per (split-merged row, 4 channels).  Rows: [H][na * N + T], the
 // anchor frames' tokens, then the extra tokens'.
+// ostride: output elements per token (H D; 2 H D when the output holds O_soft and
+// g (.) O_lin side by side, the second half then written as zeros: anchor rows have
+// no linear term).
 template <int D, bool F32OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_O,
                                                       const float* __restrict__ part_ml, int F,
-                                                      int N, int T, int H, int na, int nsplit, void* O) {
+                                                      int N, int T, int H, int na, int nsplit, void* O,
+                                                      int ostride) {
   const int R = na * N + T;
   const size_t rows = (size_t)H * R;
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1242,13 +1290,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
   const float inv = 1.f / l;
   const size_t tok = rr < na * N ? (size_t)(rr < N ? 0 : F - 1) * N + rr % N : (size_t)F * N + (rr - na * N);
-  const size_t off = tok * H * D + (size_t)h * D + 4 * c4;
+  const size_t off = tok * ostride + (size_t)h * D + 4 * c4;
   if constexpr (F32OUT) {
     *reinterpret_cast<float4*>(static_cast<float*>(O) + off) =
         make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   } else {
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(O) + off) =
         make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+    if (ostride != H * D) *reinterpret_cast<uint2*>(static_cast<uint16_t*>(O) + off + (size_t)H * D) = make_uint2(0, 0);
   }
 }
 
@@ -1396,21 +1445,24 @@ static hipError_t attn_f32(const AttnArgs& a, hipStream_t st) {
   return attn_launch(&attn_kernel<D, 0>, 2 * AttnCfg<D, 0>::STAGE, &done, a, st, 256);
 }
 template <int D, int PREC>
-static hipError_t attn_lds(const AttnArgs& a, hipStream_t st) {
+static hipError_t attn_lds(const AttnArgs& a, hipStream_t st, bool split) {
+  constexpr int lds = kLdsStages * LdsCfg<D, PREC>::STAGE;
+  if (split) {   // (no extra tokens in this form)
+    static bool done_s = false;
+    return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, true>, lds, &done_s, a, st, 64 * kLdsWaves);
+  }
   if (a.T > 0) {
     static bool done_x = false;
-    return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, true>, kLdsStages * LdsCfg<D, PREC>::STAGE, &done_x,
-                       a, st, 64 * kLdsWaves);
+    return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, true, false>, lds, &done_x, a, st, 64 * kLdsWaves);
   }
   static bool done = false;
-  return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false>, kLdsStages * LdsCfg<D, PREC>::STAGE, &done, a,
-                     st, 64 * kLdsWaves);
+  return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, false>, lds, &done, a, st, 64 * kLdsWaves);
 }
 
 hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, const uint16_t* vt,
                        const uint8_t* q8, const uint8_t* k8, const float* amax, int F, int N, int H,
                        int D, void* O, float* part_O, float* part_ml, const uint16_t* W,
-                       int T, const uint16_t* vtx, hipStream_t st) {
+                       int T, const uint16_t* vtx, int split, hipStream_t st) {
   AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.vt = vt; a.q8 = q8; a.k8 = k8; a.amax = amax;
   a.O = O; a.part_O = part_O; a.part_ml = part_ml;
@@ -1421,6 +1473,8 @@ hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, co
   // the fp32 kernel has neither the fused readout nor extra tokens
   if (prec == 0 && (W != nullptr || T != 0)) return hipErrorInvalidValue;
   if (T < 0 || (T > 0 && vtx == nullptr)) return hipErrorInvalidValue;
+  // split output: the readout weights are needed, and no extra tokens
+  if (split && (W == nullptr || T != 0 || prec == 0)) return hipErrorInvalidValue;
   a.F = F; a.N = N; a.H = H;
   attn_split_plan(F, &a.nsplit, &a.fs);
   a.na = F >= 2 ? 2 : 1;
@@ -1430,18 +1484,20 @@ hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, co
     if (D == 64) return attn_f32<64>(a, st);
     if (D == 128) return attn_f32<128>(a, st);
   } else if (prec == 1) {
-    if (D == 32) return attn_lds<32, 1>(a, st);
-    if (D == 64) return attn_lds<64, 1>(a, st);
-    if (D == 128) return attn_lds<128, 1>(a, st);
+    if (D == 32) return attn_lds<32, 1>(a, st, split != 0);
+    if (D == 64) return attn_lds<64, 1>(a, st, split != 0);
+    if (D == 128) return attn_lds<128, 1>(a, st, split != 0);
   } else if (prec == 2) {
-    if (D == 64) return attn_lds<64, 2>(a, st);
-    if (D == 128) return attn_lds<128, 2>(a, st);
+    if (D == 64) return attn_lds<64, 2>(a, st, split != 0);
+    if (D == 128) return attn_lds<128, 2>(a, st, split != 0);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_combine(int prec, const float* part_O, const float* part_ml, int F, int N, int T,
-                          int H, int D, void* O, hipStream_t st) {
+                          int H, int D, void* O, int split, hipStream_t st) {
+  if (split && prec == 0) return hipErrorInvalidValue;
+  const int ostride = (split ? 2 : 1) * H * D;
   int nsplit, fs;
   attn_split_plan(F, &nsplit, &fs);
   const int na = F >= 2 ? 2 : 1;
@@ -1451,10 +1507,10 @@ hipError_t launch_combine(int prec, const float* part_O, const float* part_ml, i
   if (D == DD) {                                                                                       \
     if (prec == 0)                                                                                     \
       hipLaunchKernelGGL((combine_kernel<DD, true>), grid, dim3(256), 0, st, part_O, part_ml, F, N, T, \
-                         H, na, nsplit, O);                                                            \
+                         H, na, nsplit, O, ostride);                                                   \
     else                                                                                               \
       hipLaunchKernelGGL((combine_kernel<DD, false>), grid, dim3(256), 0, st, part_O, part_ml, F, N,   \
-                         T, H, na, nsplit, O);                                                         \
+                         T, H, na, nsplit, O, ostride);                                                \
     return hipGetLastError();                                                                          \
   }
   VDN_COMB(32) VDN_COMB(64) VDN_COMB(128)

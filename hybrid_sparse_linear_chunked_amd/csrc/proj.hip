@@ -1,0 +1,153 @@
+// Output projections of the two branches, as one bf16 GEMM on the matrix cores:
+//   Y[M, N] = A[M, K] B[N, K]^T,   fp32 accumulation, bf16 out,
+// with A = [O_soft | g (.) O_lin] per token (K = 2 H d) and B = [W_s | W_l]
+// (arXiv abstract page, Abstract; ananclaw note, section 一、方法拆解: separate
+// output projections of the two branches, learnable gates between them).
+//
+// Workgroup tile 256 (M) x 256 (N), 8 waves, K in steps of 64.  Both operand tiles
+// go global -> LDS by 16-byte direct loads (no staging registers) into rows with
+// one 16-byte padding chunk each (144-byte pitch), so 16 consecutive rows read at
+// one chunk hit 16 distinct bank groups; two LDS stages, one barrier per step.
+// Each wave computes Y^T for 64 rows of B (N) x 128 rows of A (M): the MFMA's A
+// operand is a 32-row block of B, its B operand a 32-row block of A, so each lane
+// ends with 4 consecutive output columns (n) of one output row (m), stored as
+// 8 bytes.  Blocks walk the tile list XCD-contiguously, n fastest, so the N tiles
+// of one M tile run on one XCD and share its L2 for the A rows.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace vdn {
+
+namespace {
+
+constexpr int PJ_TM = 256, PJ_TN = 256, PJ_TK = 64;   // workgroup tile
+constexpr int PJ_NW = 8;                               // waves per workgroup
+constexpr int PJ_PITCH = 16 * 9;                       // LDS row: 8 data chunks + 1 pad
+constexpr int PJ_OPER = 256 * PJ_PITCH;                // one operand tile in LDS (36 KiB)
+constexpr int PJ_STAGE = 2 * PJ_OPER;                  // A tile + B tile
+constexpr int PJ_LOADS = 256 * 9 / 64;                 // 36 wave-wide direct loads per operand tile
+constexpr int PJ_LX = (PJ_LOADS + PJ_NW - 1) / PJ_NW;  // per wave (the last partly idle)
+constexpr int PJ_LDS = 2 * PJ_STAGE;                   // 144 KiB
+
+// (the launcher checks K % 64 == 0, N % 8 == 0, M, N, K > 0 and 2*K*256 < 2^32)
+__global__ __launch_bounds__(64 * PJ_NW, 1) void proj_kernel(const uint16_t* __restrict__ A,
+                                                             const uint16_t* __restrict__ B, int M, int N,
+                                                             int K, uint16_t* __restrict__ Y) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31, hf = lane >> 5;
+
+  // this workgroup's tile: the blocks one XCD receives (every 8th) take a
+  // contiguous run of the tile list
+  const int tn_count = (N + PJ_TN - 1) / PJ_TN, tm_count = (M + PJ_TM - 1) / PJ_TM;
+  const int T = tm_count * tn_count;
+  const int b = blockIdx.x, q8 = T >> 3, m8 = T & 7, r = b & 7;
+  const int t = r * q8 + min(r, m8) + (b >> 3);
+  const int m0 = PJ_TM * (t / tn_count), n0 = PJ_TN * (t % tn_count);
+  const int wn = w & 3, wm = w >> 2;                   // wave: B rows 64 wn.., A rows 128 wm..
+
+  // direct loads: load x of this wave fills LDS chunk q = 64 (x NW + w) + lane of
+  // an operand tile, i.e. row q / 9, chunk q % 9 (the padding chunk re-reads the
+  // row's last chunk)
+  uint32_t off[PJ_LX];
+#pragma unroll
+  for (int x = 0; x < PJ_LX; ++x) {
+    const int q = 64 * (x * PJ_NW + w) + lane;
+    const int row = q / 9, c = min(q % 9, 7);
+    off[x] = (uint32_t)row * (uint32_t)(2 * K) + 16u * c;
+  }
+  // rows past M (N) read zeros: a tile's resource ends right after its last valid
+  // row's 128 bytes of the current K step
+  const int va = min(PJ_TM, M - m0), vb = min(PJ_TN, N - n0);
+  const uint32_t a_bytes = (uint32_t)(va - 1) * (uint32_t)(2 * K) + 2 * PJ_TK;
+  const uint32_t b_bytes = (uint32_t)(vb - 1) * (uint32_t)(2 * K) + 2 * PJ_TK;
+  const uint16_t* a_base = A + (size_t)m0 * K;
+  const uint16_t* b_base = B + (size_t)n0 * K;
+  auto issue = [&](int stage, int kk) {
+    unsigned char* sb = smem + stage * PJ_STAGE;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + (size_t)kk * PJ_TK, a_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + (size_t)kk * PJ_TK, b_bytes);
+#pragma unroll
+    for (int x = 0; x < PJ_LX; ++x) {
+      if (x * PJ_NW + w >= PJ_LOADS) break;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_ptr)(sb + 1024 * (x * PJ_NW + w)), 16, off[x], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_ptr)(sb + PJ_OPER + 1024 * (x * PJ_NW + w)), 16, off[x],
+                                               0, 0, 0);
+    }
+  };
+
+  floatx16 acc[2][4];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = floatx16{};
+
+  const int nk = K / PJ_TK;
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kk = 0; kk < nk; ++kk) {
+    if (kk + 1 < nk) issue((kk + 1) & 1, kk + 1);
+    const unsigned char* sa = smem + (kk & 1) * PJ_STAGE;
+    const unsigned char* sw = sa + PJ_OPER;
+#pragma unroll
+    for (int s = 0; s < PJ_TK / 16; ++s) {
+      bf16x8 wf[2], af[4];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        wf[nb] = *reinterpret_cast<const bf16x8*>(sw + (64 * wn + 32 * nb + j) * PJ_PITCH + 16 * (2 * s + hf));
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        af[mb] = *reinterpret_cast<const bf16x8*>(sa + (128 * wm + 32 * mb + j) * PJ_PITCH + 16 * (2 * s + hf));
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma_bf16(wf[nb], af[mb], acc[nb][mb]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next step landed
+    __syncthreads();                 // ... and every wave's; this step's reads done
+  }
+
+  // lane (j, hf), element 4 g + e of block (nb, mb): output row m = m0 + 128 wm +
+  // 32 mb + j, column n = n0 + 64 wn + 32 nb + 8 g + 4 hf + e
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int m = m0 + 128 * wm + 32 * mb + j;
+    if (m >= M) continue;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + 64 * wn + 32 * nb + 8 * g + 4 * hf;
+        if (n < N) {
+          const floatx16& c = acc[nb][mb];
+          *reinterpret_cast<uint2*>(Y + (size_t)m * N + n) =
+              make_uint2(pack_bf16x2(c[4 * g + 0], c[4 * g + 1]), pack_bf16x2(c[4 * g + 2], c[4 * g + 3]));
+        }
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_proj(const uint16_t* A, const uint16_t* B, int M, int N, int K, uint16_t* Y, hipStream_t st) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % PJ_TK != 0 || N % 8 != 0) return hipErrorInvalidValue;
+  if ((long long)PJ_TM * 2 * K >= (1LL << 32)) return hipErrorInvalidValue;   // 32-bit buffer offsets
+  static bool attr_done = false;   // benign race: every caller sets the same value
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&proj_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, PJ_LDS);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  const long long tiles = (long long)((M + PJ_TM - 1) / PJ_TM) * ((N + PJ_TN - 1) / PJ_TN);
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(proj_kernel, dim3((unsigned)tiles), dim3(64 * PJ_NW), PJ_LDS, st, A, B, M, N, K, Y);
+  return hipGetLastError();
+}
+
+}  // namespace vdn

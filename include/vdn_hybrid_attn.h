@@ -102,6 +102,31 @@ int vdn_hybrid_attn_mixed(const void* q, const void* k, const void* v,
                           int F, int N, int T, int H, int d, int precision,
                           void* O, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The layer followed by the two branches' separate output projections (arXiv
+ * abstract page, Abstract; ananclaw note, section 一、方法拆解: separate output
+ * projections and learnable gates calibrate the two branches):
+ *     Y = O_soft W_s^T + (g (.) O_lin) W_l^T,
+ * with O_soft, O_lin per token flattened head-major to H*d values and g the
+ * per-(head, channel) gate of vdn_hybrid_attn (W_s = W_l = W gives vdn_hybrid_attn's
+ * O times W^T; a gate on the projected output folds into W_l's rows).
+ * q, k, v: [F, N, H, d] bf16; beta: [F, H]; gate: [H, d] fp32;
+ * Wp: [D, 2*H*d] bf16 row-major, [W_s | W_l] (row n: W_s[n, :] then W_l[n, :]);
+ * Y: [F*N, D] bf16 (fp32 accumulation).  precision VDN_PREC_BF16 or
+ * VDN_PREC_BF16_FP8QK (fp32: VDN_ERR_UNSUPPORTED); D a multiple of 8.  The
+ * workspace (vdn_workspace_bytes_proj bytes) also holds [O_soft | g (.) O_lin] as
+ * bf16 [F*N][2][H][d]. */
+size_t vdn_workspace_bytes_proj(int F, int N, int H, int d, int D, int precision);
+int vdn_hybrid_attn_proj(const void* q, const void* k, const void* v,
+                         const float* beta, const float* gate, const void* Wp,
+                         int F, int N, int H, int d, int D, int precision,
+                         void* Y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The projection GEMM alone: Y[M, N] = A[M, K] B[N, K]^T, bf16 row-major
+ * operands and output, fp32 accumulation (the product vdn_hybrid_attn_proj takes
+ * with A = [O_soft | g (.) O_lin], B = Wp).  K a multiple of 64, N a multiple of 8
+ * (else VDN_ERR_UNSUPPORTED).  No workspace. */
+int vdn_out_proj(const void* A, const void* B, int M, int K, int N, void* Y, void* stream);
+
 /* Softmax branch alone (part (a)): O_soft[i, n, h] = sum over tokens (j, m) of
  * the key frames of query frame i of softmax_{(j,m)}(q_{i,n,h} . k_{j,m,h} / sqrt(d))
  * v_{j,m,h}, with the window + anchor frame sets of the sd114.wiki article,
@@ -160,7 +185,8 @@ int vdn_schedule(int F, int* table, int cap);
 #define VDN_STAGE_READOUT  6   /* linear readout (+ gated merge in the fp32 layer; the
                                   readout of vdn_vda_linear)                            */
 #define VDN_STAGE_QUANT    7   /* fp8 quantiser of q and k                               */
-#define VDN_NUM_STAGES     8
+#define VDN_STAGE_PROJ     8   /* output projections (vdn_hybrid_attn_proj, vdn_out_proj) */
+#define VDN_NUM_STAGES     9
 
 /* Measurement aid for the calling thread: while set, every entry point records
  * the hipEvent_t `before` on its stream immediately before it enqueues the
