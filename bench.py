@@ -160,6 +160,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra-tokens", type=int, default=0, metavar="T",
                     help="append T text / audio tokens to the layer's sequence (no CPU baseline)")
+    ap.add_argument("--out-proj", type=int, default=0, metavar="D",
+                    help="follow the layer with the two branches' output projections to D channels "
+                         "(no CPU baseline)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (a known-size kernel "
                          "that calibrates the HBM byte counters), then exit")
@@ -190,6 +193,10 @@ def main():
     t0 = time.perf_counter()
 
     T = args.extra_tokens
+    Dp = args.out_proj
+    if T and Dp:
+        print("bench.py: --extra-tokens and --out-proj are separate workloads", file=sys.stderr)
+        sys.exit(2)
 
     def gen(name):
         out = torch.empty((F, N, H, d), dtype=torch.bfloat16)
@@ -204,8 +211,14 @@ def main():
     beta = torch.from_numpy(vdn_synth.beta(F, H)).to(dev)
     gate = torch.from_numpy(vdn_synth.gate(H, d)).to(dev)
     O = torch.empty_like(q)
-    ws = (vdn.new_workspace_mixed(F, N, T, H, d, p, device=dev) if T > 0
-          else vdn.new_workspace(F, N, H, d, p, device=dev))
+    if T > 0:
+        ws = vdn.new_workspace_mixed(F, N, T, H, d, p, device=dev)
+    elif Dp > 0:
+        ws = vdn.new_workspace_proj(F, N, H, d, Dp, p, device=dev)
+        Wp = torch.from_numpy(vdn_synth.proj_weights(Dp, H * d)).to(torch.bfloat16).to(dev)
+        Y = torch.empty((F * N, Dp), dtype=torch.bfloat16, device=dev)
+    else:
+        ws = vdn.new_workspace(F, N, H, d, p, device=dev)
     # the video tokens as [F, N, H, d] (the first F*N tokens when there are extras)
     qv, kv, vv = (x[:F * N].view(F, N, H, d) for x in (q, k, v)) if T > 0 else (q, k, v)
     torch.cuda.synchronize()
@@ -213,7 +226,9 @@ def main():
           f"{ws.numel() / 2**30:.2f} GiB", file=sys.stderr, flush=True)
 
     def step():
-        if T > 0:
+        if Dp > 0:
+            vdn.hybrid_attn_proj(q, k, v, beta, gate, Wp, precision=p, out=Y, workspace=ws)
+        elif T > 0:
             vdn.hybrid_attn_mixed(q, k, v, beta, gate, F, N, precision=p, out=O, workspace=ws)
         else:
             vdn.hybrid_attn(q, k, v, beta, gate, precision=p, out=O, workspace=ws)
@@ -226,7 +241,7 @@ def main():
     # stages the layer runs in this precision: the quantiser only with fp8 q.k; the
     # bf16 and fp8 layers run the readout and merge in the attention kernel
     run = [st for st, name in enumerate(vdn.STAGES)
-           if (name != "quant" or prec == "bf16_fp8qk") and name not in ("readout", "proj")]
+           if (name != "quant" or prec == "bf16_fp8qk") and name != "readout" and (name != "proj" or Dp > 0)]
     ev = {(s, st): (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for s in range(args.steps) for st in run}
     for pair in ev.values():       # torch creates the HIP event on its first record
@@ -256,6 +271,8 @@ def main():
           file=sys.stderr, flush=True)
 
     work = algorithmic_work(F, N, H, d, T)
+    proj_flop = 2.0 * F * N * Dp * 2 * H * d       # [O_soft | g O_lin] [W_s | W_l]^T
+    work["total"] += proj_flop
     attn_ms = stages["attn"]
     kflop = work["soft"] + work["readout"]      # softmax branch + the fused W q
     if prec == "bf16_fp8qk":
@@ -295,15 +312,22 @@ def main():
         "metric": METRIC, "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": cfg["workload"] + (f"_with_{T}_text_tokens" if T else ""), "F": F, "N": N,
-                   "H": H, "d": d, "precision": prec, "frame_pairs": work["P"], "extra_tokens": T},
+        "config": {"workload": cfg["workload"] + (f"_with_{T}_text_tokens" if T else "")
+                   + (f"_with_out_proj_{Dp}" if Dp else ""), "F": F, "N": N, "H": H, "d": d,
+                   "precision": prec, "frame_pairs": work["P"], "extra_tokens": T, "out_proj": Dp},
         "tflops": round(work["total"] / (ms * 1e-3) / 1e12, 2),
         "layer_flop": work["total"],
         "roofline": roofline,
         "readout": readout,
         "stages_ms": {k2: round(v2, 4) for k2, v2 in stages.items()},
     }
-    if not args.no_cpu_baseline and T == 0:
+    if Dp > 0:
+        pj_ms = stages["proj"]
+        pj = proj_flop / (pj_ms * 1e-3) / 1e12
+        result["proj"] = {"bound": "mfma", "achieved": round(pj, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(pj / PEAK_BF16_TFLOPS, 4), "kernel": "proj_kernel",
+                          "flop_per_launch": proj_flop, "kernel_ms": round(pj_ms, 3)}
+    if not args.no_cpu_baseline and T == 0 and Dp == 0:
         print("[bench] timing the oracle on a bounded sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(F, N, H, d)
     print(json.dumps(result), flush=True)

@@ -8,6 +8,8 @@
 // go global -> LDS by 16-byte direct loads (no staging registers) into rows with
 // one 16-byte padding chunk each (144-byte pitch), so 16 consecutive rows read at
 // one chunk hit 16 distinct bank groups; two LDS stages, one barrier per step.
+// Inside a step the operand fragments of sub-step s + 1 are read while the MFMAs
+// of sub-step s run, and each sub-step issues its share of the next step's loads.
 // Each wave computes Y^T for 64 rows of B (N) x 128 rows of A (M): the MFMA's A
 // operand is a 32-row block of B, its B operand a 32-row block of A, so each lane
 // ends with 4 consecutive output columns (n) of one output row (m), stored as
@@ -47,7 +49,10 @@ __global__ __launch_bounds__(64 * PJ_NW, 1) void proj_kernel(const uint16_t* __r
   const int T = tm_count * tn_count;
   const int b = blockIdx.x, q8 = T >> 3, m8 = T & 7, r = b & 7;
   const int t = r * q8 + min(r, m8) + (b >> 3);
-  const int m0 = PJ_TM * (t / tn_count), n0 = PJ_TN * (t % tn_count);
+  // (the division runs on the vector unit; the tile origin is block-uniform, and
+  // the buffer resources built from it must live in scalar registers)
+  const int m0 = __builtin_amdgcn_readfirstlane(PJ_TM * (t / tn_count));
+  const int n0 = __builtin_amdgcn_readfirstlane(PJ_TN * (t % tn_count));
   const int wn = w & 3, wm = w >> 2;                   // wave: B rows 64 wn.., A rows 128 wm..
 
   // direct loads: load x of this wave fills LDS chunk q = 64 (x NW + w) + lane of
@@ -67,12 +72,13 @@ __global__ __launch_bounds__(64 * PJ_NW, 1) void proj_kernel(const uint16_t* __r
   const uint32_t b_bytes = (uint32_t)(vb - 1) * (uint32_t)(2 * K) + 2 * PJ_TK;
   const uint16_t* a_base = A + (size_t)m0 * K;
   const uint16_t* b_base = B + (size_t)n0 * K;
-  auto issue = [&](int stage, int kk) {
+  auto issue = [&](int stage, int kk, int x0, int x1) {
     unsigned char* sb = smem + stage * PJ_STAGE;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + (size_t)kk * PJ_TK, a_bytes);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + (size_t)kk * PJ_TK, b_bytes);
 #pragma unroll
     for (int x = 0; x < PJ_LX; ++x) {
+      if (x < x0 || x >= x1) continue;
       if (x * PJ_NW + w >= PJ_LOADS) break;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_ptr)(sb + 1024 * (x * PJ_NW + w)), 16, off[x], 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_ptr)(sb + PJ_OPER + 1024 * (x * PJ_NW + w)), 16, off[x],
@@ -87,26 +93,36 @@ __global__ __launch_bounds__(64 * PJ_NW, 1) void proj_kernel(const uint16_t* __r
     for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = floatx16{};
 
   const int nk = K / PJ_TK;
-  issue(0, 0);
+  constexpr int NS = PJ_TK / 16;                       // 16-wide K sub-steps per step
+  issue(0, 0, 0, PJ_LX);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kk = 0; kk < nk; ++kk) {
-    if (kk + 1 < nk) issue((kk + 1) & 1, kk + 1);
-    const unsigned char* sa = smem + (kk & 1) * PJ_STAGE;
+  bf16x8 wf[2][2], af[2][4];
+  auto read = [&](const unsigned char* sa, int s, int buf) {
     const unsigned char* sw = sa + PJ_OPER;
 #pragma unroll
-    for (int s = 0; s < PJ_TK / 16; ++s) {
-      bf16x8 wf[2], af[4];
+    for (int nb = 0; nb < 2; ++nb)
+      wf[buf][nb] = *reinterpret_cast<const bf16x8*>(sw + (64 * wn + 32 * nb + j) * PJ_PITCH + 16 * (2 * s + hf));
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      af[buf][mb] = *reinterpret_cast<const bf16x8*>(sa + (128 * wm + 32 * mb + j) * PJ_PITCH + 16 * (2 * s + hf));
+  };
+  for (int kk = 0; kk < nk; ++kk) {
+    const bool ld = kk + 1 < nk;
+    const unsigned char* sa = smem + (kk & 1) * PJ_STAGE;
+    read(sa, 0, 0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): sub-step s's fragments
+      if (s + 1 < NS) read(sa, s + 1, (s + 1) & 1);
+      // this sub-step's share of the next step's loads
+      if (ld) issue((kk + 1) & 1, kk + 1, s * PJ_LX / NS, (s + 1) * PJ_LX / NS);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
-        wf[nb] = *reinterpret_cast<const bf16x8*>(sw + (64 * wn + 32 * nb + j) * PJ_PITCH + 16 * (2 * s + hf));
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        af[mb] = *reinterpret_cast<const bf16x8*>(sa + (128 * wm + 32 * mb + j) * PJ_PITCH + 16 * (2 * s + hf));
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma_bf16(wf[nb], af[mb], acc[nb][mb]);
+        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma_bf16(wf[s & 1][nb], af[s & 1][mb], acc[nb][mb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next step landed
     __syncthreads();                 // ... and every wave's; this step's reads done
