@@ -9,7 +9,7 @@
 // one 16-byte padding chunk each (144-byte pitch), so 16 consecutive rows read at
 // one chunk hit 16 distinct bank groups; two LDS stages, one barrier per step.
 // Inside a step the operand fragments of sub-step s + 1 are read while the MFMAs
-// of sub-step s run, and each sub-step issues its share of the next step's loads.
+// of sub-step s run, and the first two sub-steps issue the next step's loads.
 // Each wave computes Y^T for 64 rows of B (N) x 128 rows of A (M): the MFMA's A
 // operand is a 32-row block of B, its B operand a 32-row block of A, so each lane
 // ends with 4 consecutive output columns (n) of one output row (m), stored as
@@ -115,8 +115,9 @@ __global__ __launch_bounds__(64 * PJ_NW, 1) void proj_kernel(const uint16_t* __r
     for (int s = 0; s < NS; ++s) {
       __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): sub-step s's fragments
       if (s + 1 < NS) read(sa, s + 1, (s + 1) & 1);
-      // this sub-step's share of the next step's loads
-      if (ld) issue((kk + 1) & 1, kk + 1, s * PJ_LX / NS, (s + 1) * PJ_LX / NS);
+      // the next step's loads, half in each of the first two sub-steps (measured
+      // 2-3 % faster than all in the first, or a quarter in each)
+      if (ld && s < 2) issue((kk + 1) & 1, kk + 1, s * PJ_LX / 2, (s + 1) * PJ_LX / 2);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
