@@ -107,3 +107,40 @@ def test_argument_errors_return_before_launch(lib):
     assert lib.vdn_fp8_quantize(A, F, N, H, 32, A, A, None) == vdn.ERR_UNSUPPORTED
     assert lib.vdn_fp8_quantize(None, F, N, H, 64, A, A, None) == vdn.ERR_INVALID_ARG
     assert lib.vdn_last_hip_error() == 0
+
+
+def test_mixed_and_projection_argument_errors(lib):
+    # the extra-token and projection entry points reject bad arguments during their
+    # checks, before any device work
+    F, N, H, d, T, D = 20, 16, 2, 64, 10, 64
+    need = lib.vdn_workspace_bytes(F, N, H, d, 1)
+    need_x = lib.vdn_workspace_bytes_mixed(F, N, T, H, d, 1)
+    assert lib.vdn_workspace_bytes_mixed(F, N, 0, H, d, 1) == need
+    assert need_x > need
+    assert lib.vdn_workspace_bytes_mixed(F, N, T, H, d, 0) == 0          # fp32 has no extra tokens
+    assert lib.vdn_workspace_bytes_mixed(F, N, -1, H, d, 1) == 0
+    call = lib.vdn_hybrid_attn_mixed
+    assert call(A, A, A, A, A, F, N, T, H, d, 0, A, A, need_x, None) == vdn.ERR_UNSUPPORTED
+    assert call(A, A, A, A, A, F, N, -1, H, d, 1, A, A, need_x, None) == vdn.ERR_INVALID_ARG
+    assert call(A, None, A, A, A, F, N, T, H, d, 1, A, A, need_x, None) == vdn.ERR_INVALID_ARG
+    assert call(A, A, A, A, A, F, N, T, H, d, 1, A, A, need_x - 1, None) == vdn.ERR_WORKSPACE
+    assert call(A, A, A, A, A, F, N, 1 << 30, H, d, 1, A, A, need_x, None) == vdn.ERR_UNSUPPORTED
+
+    need_p = lib.vdn_workspace_bytes_proj(F, N, H, d, D, 1)
+    assert need_p >= need + F * N * 2 * H * d * 2
+    assert lib.vdn_workspace_bytes_proj(F, N, H, d, D, 0) == 0            # bf16 only
+    assert lib.vdn_workspace_bytes_proj(F, N, H, d, 12, 1) == 0           # D a multiple of 8
+    call = lib.vdn_hybrid_attn_proj
+    assert call(A, A, A, A, A, A, F, N, H, d, D, 0, A, A, need_p, None) == vdn.ERR_UNSUPPORTED
+    assert call(A, A, A, A, A, A, F, N, H, d, 12, 1, A, A, need_p, None) == vdn.ERR_UNSUPPORTED
+    assert call(A, A, A, A, A, None, F, N, H, d, D, 1, A, A, need_p, None) == vdn.ERR_INVALID_ARG
+    assert call(A, A, A, A, A, A + 8, F, N, H, d, D, 1, A, A, need_p, None) == vdn.ERR_INVALID_ARG
+    assert call(A, A, A, A, A, A, F, N, H, d, D, 1, A, A, need_p - 1, None) == vdn.ERR_WORKSPACE
+
+    gemm = lib.vdn_out_proj
+    assert gemm(A, A, 100, 96, 64, A, None) == vdn.ERR_UNSUPPORTED      # K a multiple of 64
+    assert gemm(A, A, 100, 128, 60, A, None) == vdn.ERR_UNSUPPORTED     # N a multiple of 8
+    assert gemm(A, A, 0, 128, 64, A, None) == vdn.ERR_INVALID_ARG
+    assert gemm(None, A, 100, 128, 64, A, None) == vdn.ERR_INVALID_ARG
+    assert gemm(A, A, 100, 128, 64, A + 4, None) == vdn.ERR_INVALID_ARG
+    assert lib.vdn_last_hip_error() == 0
