@@ -167,7 +167,7 @@ def hybrid_attn(q, k, v, beta, gate, precision=None, out=None, workspace=None):
     ws = _workspace(F, N, H, d, prec, q.device, workspace)
     st = load().vdn_hybrid_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
                                 gate.data_ptr(), F, N, H, d, prec, O.data_ptr(), ws.data_ptr(),
-                                ws.numel(), _stream())
+                                ws.numel() * ws.element_size(), _stream())
     _check(st, "vdn_hybrid_attn")
     return O
 
@@ -207,7 +207,7 @@ def hybrid_attn_mixed(q, k, v, beta, gate, F, N, precision=None, out=None, works
         raise VdnError(ERR_WORKSPACE, "workspace")
     st = load().vdn_hybrid_attn_mixed(q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
                                       gate.data_ptr(), F, N, T, H, d, prec, O.data_ptr(),
-                                      workspace.data_ptr(), workspace.numel(), _stream())
+                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream())
     _check(st, "vdn_hybrid_attn_mixed")
     return O
 
@@ -237,9 +237,12 @@ def hybrid_attn_proj(q, k, v, beta, gate, Wp, precision=None, out=None, workspac
     _check_io("out", Y, torch.bfloat16, (F * N, D))
     if workspace is None:
         workspace = new_workspace_proj(F, N, H, d, D, prec, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    if wbytes < int(load().vdn_workspace_bytes_proj(F, N, H, d, D, prec)):
+        raise VdnError(ERR_WORKSPACE, "workspace")
     st = load().vdn_hybrid_attn_proj(q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(), gate.data_ptr(),
                                      Wp.data_ptr(), F, N, H, d, D, prec, Y.data_ptr(), workspace.data_ptr(),
-                                     workspace.numel(), _stream())
+                                     wbytes, _stream())
     _check(st, "vdn_hybrid_attn_proj")
     return Y
 
@@ -267,7 +270,7 @@ def softmax_branch(q, k, v, precision=None, out=None, workspace=None):
     _check_io("out", O, dt, (F, N, H, d))
     ws = _workspace(F, N, H, d, prec, q.device, workspace)
     st = load().vdn_softmax_branch(q.data_ptr(), k.data_ptr(), v.data_ptr(), F, N, H, d, prec,
-                                   O.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
+                                   O.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream())
     _check(st, "vdn_softmax_branch")
     return O
 
@@ -286,7 +289,7 @@ def vda_states(k, v, beta, precision=None, workspace=None):
     Sb = torch.empty_like(Sf)
     ws = _workspace(F, N, H, d, prec, k.device, workspace)
     st = load().vdn_vda_states(k.data_ptr(), v.data_ptr(), beta.data_ptr(), F, N, H, d, prec,
-                               Sf.data_ptr(), Sb.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
+                               Sf.data_ptr(), Sb.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream())
     _check(st, "vdn_vda_states")
     return Sf, Sb
 
@@ -303,7 +306,7 @@ def vda_linear(q, S_fwd, S_bwd, precision=None, workspace=None):
     O = torch.empty_like(q)
     ws = _workspace(F, N, H, d, prec, q.device, workspace)
     st = load().vdn_vda_linear(q.data_ptr(), S_fwd.data_ptr(), S_bwd.data_ptr(), F, N, H, d, prec,
-                               O.data_ptr(), ws.data_ptr(), ws.numel(), _stream())
+                               O.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream())
     _check(st, "vdn_vda_linear")
     return O
 
