@@ -65,7 +65,7 @@ int check_extra(int F, int N, int T, int prec) {
 
 // Workspace carving (byte offsets).
 struct Layout {
-  size_t vt = 0, vtx = 0, G = 0, B = 0, Sf = 0, Sb = 0, W = 0, pO = 0, pml = 0, q8 = 0, k8 = 0, amax = 0;
+  size_t vt = 0, vtx = 0, px = 0, G = 0, B = 0, Sf = 0, Sb = 0, W = 0, pO = 0, pml = 0, q8 = 0, k8 = 0, amax = 0;
   size_t total = 0;
 };
 
@@ -86,6 +86,8 @@ Layout layout(int F, int N, int H, int d, int prec, int T = 0) {
   const size_t na = F >= 2 ? 2 : 1;
   L.vt = take(prec == VDN_PREC_FP32 ? 0 : static_cast<size_t>(H) * F * nb * d * 64 * 2);
   L.vtx = take(static_cast<size_t>(H) * ((static_cast<size_t>(T) + 63) / 64) * d * 64 * 2);
+  // with extra tokens: softmax state of every video query row, [H][F*N][d + 4] fp32 (16-byte rows)
+  L.px = take(T > 0 ? static_cast<size_t>(H) * F * N * (d + 4) * 4 : 0);
   L.G = take(static_cast<size_t>(F) * H * dd * 4);
   L.B = take(static_cast<size_t>(F) * H * dd * 4);
   L.Sf = take(C * H * dd * 4);
@@ -159,7 +161,8 @@ int run_softmax(const void* q, const void* k, const void* v, int F, int N, int H
   const int kprec = prec == VDN_PREC_FP32 ? 0 : (prec == VDN_PREC_BF16 ? 1 : 2);
   VDN_STAGE(VDN_STAGE_ATTN, st,
             vdn::launch_attn(kprec, q, k, v, ws.at<uint16_t>(L.vt), q8, k8, amax, F, N, H, d, O,
-                             ws.at<float>(L.pO), ws.at<float>(L.pml), W, T, ws.at<uint16_t>(L.vtx), split, st));
+                             ws.at<float>(L.pO), ws.at<float>(L.pml), W, T, ws.at<uint16_t>(L.vtx), split,
+                             ws.at<float>(L.px), st));
   VDN_STAGE(VDN_STAGE_COMBINE, st,
             vdn::launch_combine(prec == VDN_PREC_FP32 ? 0 : 1, ws.at<float>(L.pO), ws.at<float>(L.pml),
                                 F, N, T, H, d, O, split, st));

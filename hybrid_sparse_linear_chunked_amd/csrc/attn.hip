@@ -194,6 +194,10 @@ struct AttnArgs {
   int nbx;                // 64-key blocks of the extra tokens
   int qt_x;               // query tiles of the extra tokens' rows
   const uint16_t* vtx;    // their V^T blocks [H][nbx][D][64], laid out as vt
+  // with extra tokens: the online-softmax state of every video query row after the
+  // extra tokens' keys, [H][F*N][D + 4] (o unnormalised, m, l, 2 pad), written by the
+  // extra-token instantiation and the start of the video pass
+  float* px;
 };
 
 constexpr int BQ = 128;   // queries per work item of attn_kernel (4 waves x 32)
@@ -711,11 +715,18 @@ __device__ inline Item decode_item_x(const AttnArgs& a, int* xslot) {
   const int F = a.F, N = a.N;
   const int G = a.na * a.qt_anchor + a.qt_x;             // split-item query tiles per split
   const int na_h = G * a.nsplit;                         // split items per head
-  const int M = na_h + a.tiles_per_head;                 // items per head
-  const int b = blockIdx.x;
-  const int hh = b / M, p = b - hh * M;
-  const int q8 = M >> 3, m8 = M & 7, r = p & 7;
-  const int li = r * q8 + min(r, m8) + (p >> 3);         // item of head hh (XCD-contiguous)
+  // dispatch order: the split items of every head first (15 or so key frames
+  // each, dealt round-robin over the XCDs), then the chunk items (the extra
+  // tokens' keys only: a few tiles each), so no long item starts last
+  const int b = blockIdx.x, nsp = a.H * na_h;
+  int hh, li;
+  if (b < nsp) {
+    hh = b / na_h;
+    li = b - hh * na_h;
+  } else {
+    hh = (b - nsp) / a.tiles_per_head;
+    li = na_h + (b - nsp) - hh * a.tiles_per_head;
+  }
   it.wf = it.we = it.k_f0 = 0;
   it.h = hh;
   if (li < na_h) {
@@ -754,8 +765,8 @@ __device__ inline Item decode_item_x(const AttnArgs& a, int* xslot) {
     it.mode = 1;
     it.wf = win_first(c);
     it.we = win_end(c, F);
-    it.nslots = (it.wf > 0 ? 1 : 0) + (it.we - it.wf) + (it.we < F ? 1 : 0);
-    *xslot = it.nslots;
+    it.nslots = 0;           // the extra tokens only: the video frames follow in a second pass
+    *xslot = 0;
   }
   return it;
 }
@@ -776,10 +787,12 @@ __device__ inline Item uniform_item(Item it) {
   return it;
 }
 
-// XT: the layer has extra tokens.  SPLIT: chunk items write O_soft and g (.) O_lin
-// side by side (token stride 2 H D, the output projection's input) instead of
-// their sum.
-template <int D, int PREC, int NW, bool XT, bool SPLIT>
+// XT: the layer has extra tokens; this instantiation runs the split items with
+// them and, for chunk items, the extra tokens' keys alone, leaving the softmax
+// state in px.  XI: the chunk items' video pass that starts from that state.
+// SPLIT: chunk items write O_soft and g (.) O_lin side by side (token stride 2 H D,
+// the output projection's input) instead of their sum.
+template <int D, int PREC, int NW, bool XT, bool SPLIT, bool XI = false>
 // (waves per SIMD: 2 at d = 128, which needs ~240 registers; the fp8 path at d = 64
 // fits 128 registers, i.e. two workgroups per CU)
 __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_lds_kernel(AttnArgs a) {
@@ -922,6 +935,27 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
   // start and the first tile sets it to that tile's maximum
   float m_run = FP8 ? -INFINITY : 0.f, l_run = 0.f;
   floatx16 nm = floatx16{};      // -m in every element: the first Q.K^T accumulator input
+  if constexpr (XI) {
+    // start from the state after the extra tokens' keys (l on the first half-wave
+    // only: the two halves' partial sums are added at the end)
+    if (qvalid) {
+      const float* ps = a.px + ((size_t)h * F * N + it.q_tok0 + qi) * (D + 4);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 x4 = *reinterpret_cast<const float4*>(ps + 32 * db + 8 * g + 4 * hf);
+          o[db][4 * g + 0] = x4.x;
+          o[db][4 * g + 1] = x4.y;
+          o[db][4 * g + 2] = x4.z;
+          o[db][4 * g + 3] = x4.w;
+        }
+      m_run = ps[D];
+      l_run = hf == 0 ? ps[D + 1] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nm[r] = -m_run;
+  }
 
   // with extra tokens, tiles t >= t_x (the last ones of the key list, when the
   // item has them) are the extra tokens' 64-key blocks t - t_x, frame index F;
@@ -1035,9 +1069,10 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
     } else {
       // scores are s - m already: raise m by the excess (on the first tile, by the
       // tile maximum whatever its sign; nothing is accumulated yet to rescale)
-      if (t == 0 || __any(mx > kLazy)) {
-        const float dm = t == 0 ? mx : __builtin_fmaxf(mx, 0.f);
-        if (t != 0) {
+      const bool first = !XI && t == 0;     // nothing accumulated yet
+      if (first || __any(mx > kLazy)) {
+        const float dm = first ? mx : __builtin_fmaxf(mx, 0.f);
+        if (!first) {
           const float alpha = __builtin_amdgcn_exp2f(-dm);
           l_run *= alpha;
 #pragma unroll
@@ -1125,6 +1160,25 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
   using KArgs = const __attribute__((address_space(4))) AttnArgs*;
   KArgs kargs = (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
   asm volatile("" : "+s"(kargs));
+  if constexpr (XT) {
+    if (it.split < 0) {
+      // chunk item over the extra tokens' keys: leave the state for the video pass
+      if (qvalid) {
+        float* ps = kargs->px + ((size_t)h * F * N + it.q_tok0 + qi) * (D + 4);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4*>(ps + 32 * db + 8 * g + 4 * hf) =
+                make_float4(o[db][4 * g + 0], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+        if (hf == 0) {
+          ps[D] = m_run;
+          ps[D + 1] = l_tot;
+        }
+      }
+      return;
+    }
+  }
   const uint16_t* Wp = kargs->W;
   const bool lin = it.split < 0 && Wp != nullptr;    // workgroup-uniform
   if (lin) {
@@ -1452,8 +1506,18 @@ static hipError_t attn_lds(const AttnArgs& a, hipStream_t st, bool split) {
     return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, true>, lds, &done_s, a, st, 64 * kLdsWaves);
   }
   if (a.T > 0) {
-    static bool done_x = false;
-    return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, true, false>, lds, &done_x, a, st, 64 * kLdsWaves);
+    // the split items, and the chunk items over the extra tokens' keys (state to
+    // px); then the chunk items' video pass from that state
+    static bool done_x = false, done_i = false;
+    hipError_t e = attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, true, false>, lds, &done_x, a, st,
+                               64 * kLdsWaves);
+    if (e != hipSuccess) return e;
+    AttnArgs b = a;
+    b.na = 0;                // chunk items only
+    b.T = 0;
+    b.nbx = 0;
+    return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, false, true>, lds, &done_i, b, st,
+                       64 * kLdsWaves);
   }
   static bool done = false;
   return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, false>, lds, &done, a, st, 64 * kLdsWaves);
@@ -1462,7 +1526,7 @@ static hipError_t attn_lds(const AttnArgs& a, hipStream_t st, bool split) {
 hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, const uint16_t* vt,
                        const uint8_t* q8, const uint8_t* k8, const float* amax, int F, int N, int H,
                        int D, void* O, float* part_O, float* part_ml, const uint16_t* W,
-                       int T, const uint16_t* vtx, int split, hipStream_t st) {
+                       int T, const uint16_t* vtx, int split, float* px, hipStream_t st) {
   AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.vt = vt; a.q8 = q8; a.k8 = k8; a.amax = amax;
   a.O = O; a.part_O = part_O; a.part_ml = part_ml;
@@ -1470,9 +1534,10 @@ hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, co
   a.T = T;
   a.nbx = (T + BK - 1) / BK;
   a.vtx = vtx;
+  a.px = px;
   // the fp32 kernel has neither the fused readout nor extra tokens
   if (prec == 0 && (W != nullptr || T != 0)) return hipErrorInvalidValue;
-  if (T < 0 || (T > 0 && vtx == nullptr)) return hipErrorInvalidValue;
+  if (T < 0 || (T > 0 && (vtx == nullptr || px == nullptr))) return hipErrorInvalidValue;
   // split output: the readout weights are needed, and no extra tokens
   if (split && (W == nullptr || T != 0 || prec == 0)) return hipErrorInvalidValue;
   a.F = F; a.N = N; a.H = H;

@@ -16,7 +16,7 @@ hipError_t launch_prep(const uint16_t* k, const uint16_t* v, int F, int N, int H
 hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, const uint16_t* vt,
                        const uint8_t* q8, const uint8_t* k8, const float* amax, int F, int N, int H,
                        int D, void* O, float* part_O, float* part_ml, const uint16_t* W,
-                       int T, const uint16_t* vtx, int split, hipStream_t st);
+                       int T, const uint16_t* vtx, int split, float* px, hipStream_t st);
 hipError_t launch_combine(int prec, const float* part_O, const float* part_ml, int F, int N, int T,
                           int H, int D, void* O, int split, hipStream_t st);
 hipError_t launch_fp8_quant(const uint16_t* x, int F, int N, int H, int D, uint8_t* codes,
