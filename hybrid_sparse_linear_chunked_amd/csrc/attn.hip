@@ -1055,10 +1055,12 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
     float mx = __builtin_fmaxf(s[0][0], s[1][0]);
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[0][e]), s[1][e]);
-    mx = pair_max(mx);
+    // (a row's maximum is split over the two lanes of a pair, both in this wave:
+    // the wave-wide test gives the same answer on the per-lane parts, so the pair
+    // combine runs only when the maximum is raised)
     if constexpr (FP8) {
-      const float mt = mx * scale;
-      if (__any(mt > m_run + kLazy)) {
+      if (__any(mx * scale > m_run + kLazy)) {
+        const float mt = pair_max(mx) * scale;
         const float m_new = __builtin_fmaxf(m_run, mt);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
@@ -1071,6 +1073,7 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
       // tile maximum whatever its sign; nothing is accumulated yet to rescale)
       const bool first = !XI && t == 0;     // nothing accumulated yet
       if (first || __any(mx > kLazy)) {
+        mx = pair_max(mx);
         const float dm = first ? mx : __builtin_fmaxf(mx, 0.f);
         if (!first) {
           const float alpha = __builtin_amdgcn_exp2f(-dm);
