@@ -15,8 +15,10 @@
 // ends with 4 consecutive output columns (n) of one output row (m).  The tile
 // goes back through LDS and leaves as whole 512-byte rows, 16 bytes a lane (3 %
 // faster than each lane storing its 8-byte pieces).  Blocks walk the tile list
-// XCD-contiguously, n fastest, so the N tiles of one M tile run on one XCD and
-// share its L2 for the A rows.
+// XCD-contiguously, in groups of 4 M tiles x all N tiles (m fastest inside a
+// group), so the ~32 tiles an XCD runs at once cover about 4 M x 8 N tiles and
+// share its L2 for both operands' rows (3 % faster than all N tiles of one M tile
+// in turn, which re-fetches every B tile for each M tile).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -51,10 +53,16 @@ __global__ __launch_bounds__(64 * PJ_NW, 1) void proj_kernel(const uint16_t* __r
   const int T = tm_count * tn_count;
   const int b = blockIdx.x, q8 = T >> 3, m8 = T & 7, r = b & 7;
   const int t = r * q8 + min(r, m8) + (b >> 3);
+  // grouped order: G M tiles x all N tiles per group, m fastest inside a group
+  // (the last group takes the M tiles left over)
+  constexpr int G = 4;
+  const int grp = t / (G * tn_count), gm0 = G * grp;
+  const int gsz = min(G, tm_count - gm0);
+  const int tg = t - grp * G * tn_count;              // position inside the group
   // (the division runs on the vector unit; the tile origin is block-uniform, and
   // the buffer resources built from it must live in scalar registers)
-  const int m0 = __builtin_amdgcn_readfirstlane(PJ_TM * (t / tn_count));
-  const int n0 = __builtin_amdgcn_readfirstlane(PJ_TN * (t % tn_count));
+  const int m0 = __builtin_amdgcn_readfirstlane(PJ_TM * (gm0 + tg % gsz));
+  const int n0 = __builtin_amdgcn_readfirstlane(PJ_TN * (tg / gsz));
   const int wn = w & 3, wm = w >> 2;                   // wave: B rows 64 wn.., A rows 128 wm..
 
   // direct loads: load x of this wave fills LDS chunk q = 64 (x NW + w) + lane of
