@@ -168,7 +168,7 @@ def main():
                          "that calibrates the HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: one GPU only (asked for --gpus {args.gpus}); "
               "the layer shards by head across GPUs but no multi-GPU path is built", file=sys.stderr)
         sys.exit(2)
 
