@@ -44,6 +44,7 @@ def relF(x, ref):
     (300, 128, 200),     # ragged M and N tiles
     (513, 192, 264),
     (1024, 6144, 512),   # the layer's K at d = 128, H = 24
+    (1300, 128, 520),    # 6 M tiles: one full group of 4 and a partial one; ragged N
 ])
 def test_gemm_alone(M, K, N):
     say(f"case gemm M={M} K={K} N={N}")
