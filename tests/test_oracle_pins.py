@@ -24,7 +24,7 @@ def small_inputs(F, N, H, d, seed=0, q_std=1.0):
 
 # ---------------------------------------------------------------- partition
 
-@pytest.mark.parametrize("F", [12, 20, 22])
+@pytest.mark.parametrize("F", [12, 20, 22, 30])
 def test_partition_matches_hand_written_tables(F):
     table = load_partition(F)
     for i in range(F):
@@ -327,6 +327,54 @@ def test_states_equal_ema_closed_form(F):
     i = F // 2
     c = i // 5
     np.testing.assert_allclose(Ol[i, 3, 1], (Sf[c, 1] + Sb[c, 1]) @ q[i, 3, 1], rtol=1e-12)
+
+
+def _ema_weights(frames, beta_h, latest_first):
+    """Weight of each absorbed frame in the state after the identity-key updates
+    S <- (S + b_t V_t) / (1 + b_t) over `frames`, in absorption order: frame t
+    keeps b_t / prod(1 + b_u) over itself and every frame absorbed after it."""
+    order = sorted(frames, reverse=latest_first)
+    w = {}
+    for pos, t in enumerate(order):
+        w[t] = beta_h[t] / np.prod([1.0 + beta_h[u] for u in order[pos:]])
+    return w
+
+
+@pytest.mark.parametrize("F", [20, 22, 30])
+def test_linear_branch_closed_form_every_frame(F):
+    # Identity keys (K_t = I, N = d) turn every state into an exponential moving
+    # average of the value blocks, and a one-hot query e_m reads column m of
+    # S_fwd + S_bwd, i.e. row m of each absorbed value block, weighted as above.
+    # So O_lin of every token of every non-anchor frame has a closed form over the
+    # hand-written forward / backward sets (sd114.wiki, 双向线性注意力分支: the query
+    # reads both states and adds them; anchor frames read nothing); the one-hot
+    # index varies with frame, token and head, so a readout that took another
+    # chunk's states, another head or another query column would not match.
+    H, d = 2, 6
+    N = d
+    _, k, v, beta = _identity_key_inputs(F, H, d, seed=9)
+    q = np.zeros((F, N, H, d))
+    onehot = lambda i, n, h: (n + 3 * i + 5 * h) % d
+    for i in range(F):
+        for n in range(N):
+            for h in range(H):
+                q[i, n, h, onehot(i, n, h)] = 1.0
+    table = load_partition(F)
+    Sf, Sb = orc.vda_states(k, v, beta)
+    got = orc.linear_branch(q, Sf, Sb)
+    for i in range(F):
+        _, fwd, bwd = table[i]
+        for h in range(H):
+            wf = _ema_weights(fwd, beta[:, h], latest_first=False)
+            wb = _ema_weights(bwd, beta[:, h], latest_first=True)
+            for n in range(N):
+                m = onehot(i, n, h)
+                ref = np.zeros(d)
+                if i not in (0, F - 1):
+                    for t, w in list(wf.items()) + list(wb.items()):
+                        ref += w * v[t, m, h, :]
+                np.testing.assert_allclose(got[i, n, h], ref, rtol=1e-12, atol=1e-14)
+    assert np.abs(got).max() > 1e-2          # both directions contribute somewhere
 
 
 def test_time_reversal_swaps_directions():
