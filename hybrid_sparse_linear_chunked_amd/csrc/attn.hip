@@ -1184,6 +1184,12 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
   }
   const uint16_t* Wp = kargs->W;
   const bool lin = it.split < 0 && Wp != nullptr;    // workgroup-uniform
+  // q rows in bf16 as they are stored (the B operand of W q^T): loaded here, beside
+  // the W tile, so the readout sees q rounded once, as the standalone readout does
+  // (the resident Q fragments of the bf16 path carry log2(e)/sqrt(d) and an extra
+  // rounding; the fp8 path's are E4M3 codes)
+  constexpr int QS = D / 16;
+  bf16x8 qr[QS];
   if (lin) {
     const int chunk = it.q_tok0 / N / kChunk;      // chunk of the item's first (and every) row
     const uint16_t* wsrc = Wp + ((size_t)chunk * H + h) * (size_t)(D * D);
@@ -1197,6 +1203,10 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (lds_void_ptr)(smem + 1024 * (x * NW + w)), 16,
                                                (uint32_t)(row * 2 * D + 16 * c), 0, 0, 0);
     }
+    const uint16_t* qrow = static_cast<const uint16_t*>(kargs->q) + (size_t)(it.q_tok0 + qi) * rs + (size_t)h * D;
+#pragma unroll
+    for (int s = 0; s < QS; ++s)
+      qr[s] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hf) : bf16x8{};
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -1205,20 +1215,6 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
   float inv = 1.f / l_tot;
   if constexpr (SPLIT) {
     if (lin) {
-      constexpr int QS = D / 16;
-      bf16x8 qr[QS];
-      float us;
-      if constexpr (FP8) {
-        const uint16_t* q = static_cast<const uint16_t*>(a.q);
-#pragma unroll
-        for (int s = 0; s < QS; ++s)
-          qr[s] = qvalid ? *reinterpret_cast<const bf16x8*>(q + qoff + 16 * s + 8 * hf) : bf16x8{};
-        us = 1.f;
-      } else {
-#pragma unroll
-        for (int s = 0; s < QS; ++s) qr[s] = qb[s];
-        us = 1.f / kargs->scale_log2;
-      }
       // token stride 2 H D: O_soft at h D, g (.) O_lin at H D + h D
       uint16_t* ao = static_cast<uint16_t*>(kargs->O) + (size_t)(it.q_tok0 + qi) * (2 * rs) + (size_t)h * D;
 #pragma unroll
@@ -1236,8 +1232,7 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
                 make_uint2(pack_bf16x2(c[4 * g + 0] * inv, c[4 * g + 1] * inv),
                            pack_bf16x2(c[4 * g + 2] * inv, c[4 * g + 3] * inv));
             *reinterpret_cast<uint2*>(ao + rs + dd) =
-                make_uint2(pack_bf16x2(acc[4 * g + 0] * us, acc[4 * g + 1] * us),
-                           pack_bf16x2(acc[4 * g + 2] * us, acc[4 * g + 3] * us));
+                make_uint2(pack_bf16x2(acc[4 * g + 0], acc[4 * g + 1]), pack_bf16x2(acc[4 * g + 2], acc[4 * g + 3]));
           }
         }
       }
@@ -1245,22 +1240,6 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
     }
   }
   if (lin) {
-    // Q in bf16 as the B operand: the bf16 path's resident fragments carry the
-    // factor log2(e)/sqrt(d), taken back out of the product; the fp8 path reads q
-    constexpr int QS = D / 16;
-    bf16x8 qr[QS];
-    float us;
-    if constexpr (FP8) {
-      const uint16_t* q = static_cast<const uint16_t*>(a.q);
-#pragma unroll
-      for (int s = 0; s < QS; ++s)
-        qr[s] = qvalid ? *reinterpret_cast<const bf16x8*>(q + qoff + 16 * s + 8 * hf) : bf16x8{};
-      us = 1.f;
-    } else {
-#pragma unroll
-      for (int s = 0; s < QS; ++s) qr[s] = qb[s];
-      us = 1.f / kargs->scale_log2;
-    }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       floatx16 acc = floatx16{};
@@ -1268,7 +1247,7 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
       for (int s = 0; s < QS; ++s)
         acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(smem + (32 * db + j) * WP + 16 * (2 * s + hf)), qr[s], acc);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] = fmaf(acc[r], us, o[db][r] * inv);
+      for (int r = 0; r < 16; ++r) o[db][r] = fmaf(o[db][r], inv, acc[r]);
     }
     inv = 1.f;
   }
@@ -1479,16 +1458,12 @@ static void attn_items(AttnArgs& a) {
 }
 
 template <typename KernelFn>
-static hipError_t attn_launch(KernelFn fn, int lds, bool* attr_done, AttnArgs a, hipStream_t st,
+static hipError_t attn_launch(KernelFn fn, int lds, std::atomic<unsigned long long>* attr_done, AttnArgs a, hipStream_t st,
                               int threads, int bq = 0) {
   a.bq = bq > 0 ? bq : 32 * (threads / 64);
   attn_items(a);
-  if (!*attr_done) {     // benign race: every caller sets the same value
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    *attr_done = true;
-  }
+  hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(fn), lds, attr_done);
+  if (e != hipSuccess) return e;
   const int nitems = a.n_anchor_items + a.H * a.tiles_per_head;
   if (nitems == 0) return hipSuccess;
   hipLaunchKernelGGL(fn, dim3(nitems), dim3(threads), lds, st, a);
@@ -1498,20 +1473,20 @@ static hipError_t attn_launch(KernelFn fn, int lds, bool* attr_done, AttnArgs a,
 // fp32 I/O: the register-staged kernel; bf16 and fp8: the direct-to-LDS kernel
 template <int D>
 static hipError_t attn_f32(const AttnArgs& a, hipStream_t st) {
-  static bool done = false;
+  static std::atomic<unsigned long long> done{0};
   return attn_launch(&attn_kernel<D, 0>, 2 * AttnCfg<D, 0>::STAGE, &done, a, st, 256);
 }
 template <int D, int PREC>
 static hipError_t attn_lds(const AttnArgs& a, hipStream_t st, bool split) {
   constexpr int lds = kLdsStages * LdsCfg<D, PREC>::STAGE;
   if (split) {   // (no extra tokens in this form)
-    static bool done_s = false;
+    static std::atomic<unsigned long long> done_s{0};
     return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, true>, lds, &done_s, a, st, 64 * kLdsWaves);
   }
   if (a.T > 0) {
     // the split items, and the chunk items over the extra tokens' keys (state to
     // px); then the chunk items' video pass from that state
-    static bool done_x = false, done_i = false;
+    static std::atomic<unsigned long long> done_x{0}, done_i{0};
     hipError_t e = attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, true, false>, lds, &done_x, a, st,
                                64 * kLdsWaves);
     if (e != hipSuccess) return e;
@@ -1522,7 +1497,7 @@ static hipError_t attn_lds(const AttnArgs& a, hipStream_t st, bool split) {
     return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, false, true>, lds, &done_i, b, st,
                        64 * kLdsWaves);
   }
-  static bool done = false;
+  static std::atomic<unsigned long long> done{0};
   return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, false>, lds, &done, a, st, 64 * kLdsWaves);
 }
 

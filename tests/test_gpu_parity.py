@@ -3,8 +3,16 @@ the same seeded inputs, per branch and for the merged output.
 
 Tolerances (max over heads of the relative Frobenius error): 1e-4 fp32, 1e-2 bf16,
 5e-2 for the fp8 (E4M3 q.k) softmax variant against the unquantised oracle and
-1e-2 against the oracle fed the same E4M3 codes.  Integer work (the partition,
-the E4M3 codes) is compared bit for bit."""
+1e-2 against the oracle fed the same E4M3 codes.  The VDA states are fp32 in every
+precision (the oracle sees the same rounded k and v), so they are held to 1e-5.
+Integer work (the partition, the E4M3 codes) is compared bit for bit.
+
+In the bf16 and fp8 layers the readout and gated merge run in the softmax kernel's
+epilogue, and at these input distributions the gated linear term dominates O
+(|O_soft| is well under 1 % of |O|).  The softmax half of that fused output is
+therefore isolated on its own: with g = 0 the layer must equal the softmax branch
+bit for bit, and with a small gate (so that O_soft carries most of |O|) the layer
+must match the oracle."""
 import os
 import sys
 
@@ -59,6 +67,9 @@ def check(name, got, ref, tol):
     assert e <= tol, f"{name}: {e} > {tol}"
 
 
+STATE_TOL = 1e-5        # fp32 states from the same rounded inputs as the oracle's
+
+
 def _states_err(S, R):
     # states [C, H, d, d]: per-head relative error, max over heads
     S = S.to(torch.float64).cpu().numpy()
@@ -72,7 +83,7 @@ def compare_full(inp, got, ref, precision, soft_tol=None):
     es = _states_err(Sf, rSf)
     eb = _states_err(Sb, rSb)
     say(f"  S_fwd {es:.3e}  S_bwd {eb:.3e}")
-    assert es <= tol and eb <= tol
+    assert es <= STATE_TOL and eb <= STATE_TOL
     check("O_soft", host(Os), rOs, soft_tol or tol)
     check("O_lin", host(Ol), rOl, tol)
     check("O", host(O), rO, soft_tol or tol)
@@ -140,20 +151,76 @@ def test_identity_keys_ema_states():
         compare_full(inp, got, ref, prec)
 
 
-def test_mid_config_sampled_frames():
-    # F=45, N=1024, H=16, d=128 bf16: every head's states, sampled query frames
-    F, N, H, d = 45, 1024, 16, 128
-    say(f"case mid F={F} N={N} H={H} d={d}")
+MID = (45, 1024, 16, 128)
+
+
+@pytest.fixture(scope="module")
+def mid_layer():
+    """The F=45, N=1024, H=16, d=128 bf16 workload, every output on the host."""
+    F, N, H, d = MID
+    say(f"case mid F={F} N={N} H={H} d={d} (device)")
     inp = Inputs(F, N, H, d, "bf16")
     O, Os, Ol, Sf, Sb = run_all(inp, "bf16")
-    heads = [0, 7, 15]
-    frames = [0, 1, 4, 5, 12, 22, 37, 40, 43, 44]
-    tokens = list(range(0, N, 7))
-    rOs, rOl, rO, rSf, rSb = oracle_slices(inp, frames, heads, tokens)
-    assert _states_err(Sf[:, heads], rSf) <= 1e-2 and _states_err(Sb[:, heads], rSb) <= 1e-2
-    check("O_soft", host(Os, frames, tokens, heads), rOs, 1e-2)
-    check("O_lin", host(Ol, frames, tokens, heads), rOl, 1e-2)
-    check("O", host(O, frames, tokens, heads), rO, 1e-2)
+    out = dict(inp=inp, O=O.cpu(), Os=Os.cpu(), Ol=Ol.cpu(), Sf=Sf.cpu(), Sb=Sb.cpu())
+    del O, Os, Ol, Sf, Sb
+    return out
+
+
+@pytest.mark.parametrize("heads", [[0, 1, 2, 3], [4, 5, 6, 7], [8, 9, 10, 11], [12, 13, 14, 15]])
+def test_mid_config_full(mid_layer, heads):
+    # every frame, token and channel of four heads per case (the oracle needs about
+    # 10 s per head here), states of those heads
+    F, N, H, d = MID
+    say(f"case mid full, heads {heads}")
+    m = mid_layer
+    frames = list(range(F))
+    rOs, rOl, rO, rSf, rSb = oracle_slices(m["inp"], frames, heads)
+    es = _states_err(m["Sf"][:, heads], rSf)
+    eb = _states_err(m["Sb"][:, heads], rSb)
+    say(f"  S_fwd {es:.3e}  S_bwd {eb:.3e}")
+    assert es <= STATE_TOL and eb <= STATE_TOL
+    check("O_soft", host(m["Os"], heads=heads), rOs, 1e-2)
+    check("O_lin", host(m["Ol"], heads=heads), rOl, 1e-2)
+    check("O", host(m["O"], heads=heads), rO, 1e-2)
+
+
+# ------------------------------------------------------------------ the fused epilogue's softmax half, d = 128
+
+def _fused_softmax_half(inp, precision, frames, heads, tokens, gate_scale=3e-3):
+    """(i) g = 0: the layer equals the softmax branch bit for bit; (ii) a small gate,
+    so that O_soft carries most of |O|: the layer matches the oracle (fp8: within
+    1e-2 of the oracle fed the same E4M3 codes and 5e-2 of the unquantised one)."""
+    p = PREC[precision]
+    fp8 = precision == "bf16_fp8qk"
+    O0 = vdn.hybrid_attn(inp.dq, inp.dk, inp.dv, inp.dbeta, torch.zeros_like(inp.dgate), precision=p)
+    Os = vdn.softmax_branch(inp.dq, inp.dk, inp.dv, precision=p)
+    torch.cuda.synchronize()
+    assert torch.equal(O0.view(torch.int16), Os.view(torch.int16)), "g = 0 layer differs from the softmax branch"
+    say("  g = 0: layer == softmax branch (bitwise)")
+    del O0, Os
+    small = inp.dgate * gate_scale
+    O = vdn.hybrid_attn(inp.dq, inp.dk, inp.dv, inp.dbeta, small, precision=p)
+    torch.cuda.synchronize()
+    got = host(O, frames, tokens, heads)
+    del O
+    g = inp.gate.numpy().astype(np.float64)[heads] * np.float64(np.float32(gate_scale))
+    for quant in ((True, False) if fp8 else (False,)):
+        rOs, rOl, _, _, _ = oracle_slices(inp, frames, heads, tokens, fp8=quant)
+        rO = orc.merge(rOs, rOl, g)
+        soft_share = np.linalg.norm(rOs) / np.linalg.norm(rO)
+        lin_share = np.linalg.norm(g[None, None] * rOl) / np.linalg.norm(rO)
+        say(f"  small gate: |O_soft| / |O| = {soft_share:.3f}, |g O_lin| / |O| = {lin_share:.3f}")
+        assert soft_share >= 0.3 and lin_share >= 0.1
+        check("O (small gate)" + (" vs E4M3 oracle" if quant else ""), got, rO,
+              1e-2 if (quant or not fp8) else 5e-2)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "bf16_fp8qk"])
+def test_fused_softmax_half_mid(precision):
+    F, N, H, d = 25, 1024, 3, 128
+    say(f"case fused epilogue F={F} N={N} H={H} d={d} {precision}")
+    inp = Inputs(F, N, H, d, precision, seed=11)
+    _fused_softmax_half(inp, precision, list(range(F)), list(range(H)), None)
 
 
 def test_determinism():
@@ -208,7 +275,7 @@ def sampled_full_size(F, N, H, d, precision):
     es = _states_err(Sf[:, heads], rSf)
     eb = _states_err(Sb[:, heads], rSb)
     say(f"  S_fwd {es:.3e}  S_bwd {eb:.3e}")
-    assert es <= 1e-2 and eb <= 1e-2
+    assert es <= STATE_TOL and eb <= STATE_TOL
     check("O_soft", host(Os, frames, tokens, heads), rOs, 1e-2)
     check("O", host(O, frames, tokens, heads), rO, 1e-2)
     if fp8:
@@ -216,6 +283,9 @@ def sampled_full_size(F, N, H, d, precision):
         uOs, _, uO, _, _ = oracle_slices(inp, frames, heads, tokens, fp8=False)
         check("O_soft vs unquantised", host(Os, frames, tokens, heads), uOs, 5e-2)
         check("O vs unquantised", host(O, frames, tokens, heads), uO, 5e-2)
+    del O, Os, Sf, Sb
+    # the softmax half of the fused output, at this shape and launch configuration
+    _fused_softmax_half(inp, precision, frames, heads, tokens)
 
 
 def test_headline_config_sampled():
@@ -224,3 +294,22 @@ def test_headline_config_sampled():
 
 def test_long_stream_fp8_sampled():
     sampled_full_size(180, 4032, 24, 128, "bf16_fp8qk")
+
+
+def test_binding_rejects_aliasing():
+    # outputs must not alias inputs, and the workspace must alias neither: the
+    # binding refuses such calls before anything is launched
+    F, N, H, d = 12, 32, 2, 64
+    inp = Inputs(F, N, H, d, "bf16", seed=12)
+    with pytest.raises(ValueError):
+        vdn.hybrid_attn(inp.dq, inp.dk, inp.dv, inp.dbeta, inp.dgate, out=inp.dq)
+    with pytest.raises(ValueError):
+        vdn.softmax_branch(inp.dq, inp.dk, inp.dv, out=inp.dv)
+    need = vdn.workspace_bytes(F, N, H, d, vdn.PREC_BF16)
+    ws = torch.empty(need + inp.dq.numel() * 2, dtype=torch.uint8, device="cuda")
+    inside = ws[-inp.dq.numel() * 2:].view(torch.bfloat16).view(F, N, H, d)
+    with pytest.raises(ValueError):
+        vdn.hybrid_attn(inp.dq, inp.dk, inp.dv, inp.dbeta, inp.dgate, out=inside, workspace=ws)
+    ok = vdn.hybrid_attn(inp.dq, inp.dk, inp.dv, inp.dbeta, inp.dgate, workspace=ws[:need])
+    torch.cuda.synchronize()
+    assert ok.shape == inp.dq.shape
