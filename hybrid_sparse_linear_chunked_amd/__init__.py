@@ -126,6 +126,23 @@ def _check_io(name, x, dtype, shape=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(x.shape)}")
 
 
+def _span(x):
+    p = x.data_ptr()
+    return p, p + x.numel() * x.element_size()
+
+
+def _check_no_alias(what, x, **others):
+    """Raise if tensor `x` shares memory with any of `others` (outputs must not
+    alias inputs, and the workspace must alias neither)."""
+    a0, a1 = _span(x)
+    for name, y in others.items():
+        if y is None:
+            continue
+        b0, b1 = _span(y)
+        if a0 < b1 and b0 < a1:
+            raise ValueError(f"{what} overlaps {name}: outputs and workspace must not alias inputs")
+
+
 def _io_dtype(prec):
     torch = _torch()
     return torch.float32 if prec == PREC_FP32 else torch.bfloat16
@@ -165,6 +182,8 @@ def hybrid_attn(q, k, v, beta, gate, precision=None, out=None, workspace=None):
     O = torch.empty_like(q) if out is None else out
     _check_io("out", O, dt, (F, N, H, d))
     ws = _workspace(F, N, H, d, prec, q.device, workspace)
+    _check_no_alias("out", O, q=q, k=k, v=v, beta=beta, gate=gate, workspace=ws)
+    _check_no_alias("workspace", ws, q=q, k=k, v=v, beta=beta, gate=gate)
     st = load().vdn_hybrid_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
                                 gate.data_ptr(), F, N, H, d, prec, O.data_ptr(), ws.data_ptr(),
                                 ws.numel() * ws.element_size(), _stream())
@@ -205,6 +224,8 @@ def hybrid_attn_mixed(q, k, v, beta, gate, F, N, precision=None, out=None, works
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < need:
         raise VdnError(ERR_WORKSPACE, "workspace")
+    _check_no_alias("out", O, q=q, k=k, v=v, beta=beta, gate=gate, workspace=workspace)
+    _check_no_alias("workspace", workspace, q=q, k=k, v=v, beta=beta, gate=gate)
     st = load().vdn_hybrid_attn_mixed(q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
                                       gate.data_ptr(), F, N, T, H, d, prec, O.data_ptr(),
                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream())
@@ -240,6 +261,8 @@ def hybrid_attn_proj(q, k, v, beta, gate, Wp, precision=None, out=None, workspac
     wbytes = workspace.numel() * workspace.element_size()
     if wbytes < int(load().vdn_workspace_bytes_proj(F, N, H, d, D, prec)):
         raise VdnError(ERR_WORKSPACE, "workspace")
+    _check_no_alias("out", Y, q=q, k=k, v=v, beta=beta, gate=gate, Wp=Wp, workspace=workspace)
+    _check_no_alias("workspace", workspace, q=q, k=k, v=v, beta=beta, gate=gate, Wp=Wp)
     st = load().vdn_hybrid_attn_proj(q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(), gate.data_ptr(),
                                      Wp.data_ptr(), F, N, H, d, D, prec, Y.data_ptr(), workspace.data_ptr(),
                                      wbytes, _stream())
@@ -256,6 +279,7 @@ def out_proj(A, B, out=None):
     _check_io("B", B, torch.bfloat16, (N, K))
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device) if out is None else out
     _check_io("out", Y, torch.bfloat16, (M, N))
+    _check_no_alias("out", Y, A=A, B=B)
     _check(load().vdn_out_proj(A.data_ptr(), B.data_ptr(), M, K, N, Y.data_ptr(), _stream()), "vdn_out_proj")
     return Y
 
@@ -269,6 +293,8 @@ def softmax_branch(q, k, v, precision=None, out=None, workspace=None):
     O = _torch().empty_like(q) if out is None else out
     _check_io("out", O, dt, (F, N, H, d))
     ws = _workspace(F, N, H, d, prec, q.device, workspace)
+    _check_no_alias("out", O, q=q, k=k, v=v, workspace=ws)
+    _check_no_alias("workspace", ws, q=q, k=k, v=v)
     st = load().vdn_softmax_branch(q.data_ptr(), k.data_ptr(), v.data_ptr(), F, N, H, d, prec,
                                    O.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream())
     _check(st, "vdn_softmax_branch")
@@ -288,6 +314,7 @@ def vda_states(k, v, beta, precision=None, workspace=None):
     Sf = torch.empty((C, H, d, d), dtype=torch.float32, device=k.device)
     Sb = torch.empty_like(Sf)
     ws = _workspace(F, N, H, d, prec, k.device, workspace)
+    _check_no_alias("workspace", ws, k=k, v=v, beta=beta)
     st = load().vdn_vda_states(k.data_ptr(), v.data_ptr(), beta.data_ptr(), F, N, H, d, prec,
                                Sf.data_ptr(), Sb.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream())
     _check(st, "vdn_vda_states")
@@ -305,6 +332,7 @@ def vda_linear(q, S_fwd, S_bwd, precision=None, workspace=None):
     _check_io("S_bwd", S_bwd, torch.float32, (C, H, d, d))
     O = torch.empty_like(q)
     ws = _workspace(F, N, H, d, prec, q.device, workspace)
+    _check_no_alias("workspace", ws, q=q, S_fwd=S_fwd, S_bwd=S_bwd)
     st = load().vdn_vda_linear(q.data_ptr(), S_fwd.data_ptr(), S_bwd.data_ptr(), F, N, H, d, prec,
                                O.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream())
     _check(st, "vdn_vda_linear")

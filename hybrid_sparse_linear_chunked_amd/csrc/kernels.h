@@ -5,7 +5,25 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace vdn {
+
+// One-time opt-in of kernel `fn` to `lds` bytes of dynamic LDS on the current
+// device.  `done` holds one bit per device id (ids from 64 up set the attribute on
+// every call); the atomic makes first calls from several threads well defined,
+// and setting the same value twice is harmless.
+inline hipError_t set_max_lds_once(const void* fn, int lds, std::atomic<unsigned long long>* done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = dev >= 0 && dev < 64 ? (1ull << dev) : 0ull;
+  if (bit != 0 && (done->load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  if (bit != 0) done->fetch_or(bit, std::memory_order_release);
+  return hipSuccess;
+}
 
 // proj.hip: Y[M, N] = A[M, K] B[N, K]^T (bf16, fp32 accumulation); K % 64 == 0, N % 8 == 0
 hipError_t launch_proj(const uint16_t* A, const uint16_t* B, int M, int N, int K, uint16_t* Y, hipStream_t st);

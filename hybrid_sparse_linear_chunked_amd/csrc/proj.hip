@@ -174,13 +174,9 @@ __global__ __launch_bounds__(64 * PJ_NW, 1) void proj_kernel(const uint16_t* __r
 hipError_t launch_proj(const uint16_t* A, const uint16_t* B, int M, int N, int K, uint16_t* Y, hipStream_t st) {
   if (M <= 0 || N <= 0 || K <= 0 || K % PJ_TK != 0 || N % 8 != 0) return hipErrorInvalidValue;
   if ((long long)PJ_TM * 2 * K >= (1LL << 32)) return hipErrorInvalidValue;   // 32-bit buffer offsets
-  static bool attr_done = false;   // benign race: every caller sets the same value
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&proj_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, PJ_LDS);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  static std::atomic<unsigned long long> attr_done{0};
+  hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(&proj_kernel), PJ_LDS, &attr_done);
+  if (e != hipSuccess) return e;
   const long long tiles = (long long)((M + PJ_TM - 1) / PJ_TM) * ((N + PJ_TN - 1) / PJ_TN);
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(proj_kernel, dim3((unsigned)tiles), dim3(64 * PJ_NW), PJ_LDS, st, A, B, M, N, K, Y);

@@ -533,13 +533,9 @@ hipError_t launch_gram_f32(const float* k, const float* v, int F, int N, int H, 
 template <int D>
 static hipError_t factor_d(float* G, float* B, const float* beta, int F, int H, hipStream_t st) {
   const size_t lds = ((size_t)D * (D + 1) + 4 * D) * sizeof(float);
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&factor_kernel<D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  static std::atomic<unsigned long long> attr_done{0};
+  hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(&factor_kernel<D>), (int)lds, &attr_done);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(factor_kernel<D>, dim3(F - 2, H), dim3(FACTOR_THREADS), lds, st, G, B, beta, F, H);
   return hipGetLastError();
 }

@@ -149,21 +149,35 @@ int vdn_vda_states(const void* k, const void* v, const float* beta,
 
 /* VDA readout alone (part (b), query side): O_lin[i, n, h] = (S_fwd[c(i), h] +
  * S_bwd[c(i), h]) q[i, n, h] for non-anchor frames i (c(i) = i / 5), and 0 on the
- * first and last frame.  Ungated.  q, O_lin: [F, N, H, d] in the precision's I/O
+ * first and last frame (sd114.wiki article, section 双向线性注意力分支: a query
+ * reads the forward and the backward state and adds the two results; the anchor
+ * frames, covered by softmax over every frame, are not computed again).  Ungated.  q, O_lin: [F, N, H, d] in the precision's I/O
  * type; S_fwd, S_bwd: fp32 [C, H, d, d].  Needs no workspace beyond
  * vdn_workspace_bytes (the same workspace convention applies). */
 int vdn_vda_linear(const void* q, const float* S_fwd, const float* S_bwd,
                    int F, int N, int H, int d, int precision,
                    void* O_lin, void* workspace, size_t workspace_bytes, void* stream);
 
-/* The fp8 quantiser of VDN_PREC_BF16_FP8QK, exposed for byte-exact checks:
+/* The fp8 quantiser of VDN_PREC_BF16_FP8QK, exposed for byte-exact checks.  The
+ * pages run the softmax branch in FP8 (besthub article, section Performance
+ * Results: branch-specific Ulysses sequence parallelism and FP8; model card
+ * "Video DeltaNet: Hybrid Attention to Speed Up Video Models with Near-Lossless
+ * Quality", section Your first render: the 8nfe_tuned_fp8 configuration) without
+ * naming the format or the scaling; this library takes OCP E4M3 with one scale per
+ * head:
  * amax[h] = max |x| over head h (fp32), code = E4M3(RNE, saturating) of
  * fp32(x * fp32(448 / amax[h])) (0 where amax is 0).  x: bf16 [F, N, H, d];
  * codes: uint8 [F, N, H, d] (OCP E4M3 "FN" bit patterns); amax: fp32 [H]. */
 int vdn_fp8_quantize(const void* x, int F, int N, int H, int d,
                      unsigned char* codes, float* amax, void* stream);
 
-/* Frame partition of the layer for F frames (host only, no device work).
+/* Frame partition of the layer for F frames (host only, no device work): the
+ * softmax key frames of every query frame (sd114.wiki article, section
+ * 双向滑动窗口Softmax分支: its own chunk of five frames, the previous and the next
+ * chunk, the first and the last frame; the first and last frame see every frame)
+ * and the frames of its forward and backward states (section 双向线性注意力分支:
+ * the non-anchor frames before and after the window, so that the three sets are
+ * disjoint and together cover every frame).
  * One row of VDN_SCHED_COLS ints per group of query frames that share their
  * sets: { q_first, q_last, n_soft,  s0_first, s0_last, s1_first, s1_last,
  *         s2_first, s2_last,  fwd_first, fwd_last, bwd_first, bwd_last }
