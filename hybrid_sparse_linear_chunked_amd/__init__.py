@@ -17,7 +17,8 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libvdn_hybrid_attn.so")
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 64 << 20          # VDN_NOALLOC_SCRATCH_BYTES
 PREC_FP32, PREC_BF16, PREC_BF16_FP8QK = 0, 1, 2
 PRECISIONS = {"fp32": PREC_FP32, "bf16": PREC_BF16, "bf16_fp8qk": PREC_BF16_FP8QK}
 SCHED_COLS = 13
@@ -34,6 +35,7 @@ _SIGS = {
     "vdn_workspace_bytes_proj": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "vdn_hybrid_attn_proj": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "vdn_out_proj": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "vdn_hybrid_attn_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "vdn_hybrid_attn_mixed": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "vdn_softmax_branch": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "vdn_vda_states": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
@@ -188,6 +190,28 @@ def hybrid_attn(q, k, v, beta, gate, precision=None, out=None, workspace=None):
                                 gate.data_ptr(), F, N, H, d, prec, O.data_ptr(), ws.data_ptr(),
                                 ws.numel() * ws.element_size(), _stream())
     _check(st, "vdn_hybrid_attn")
+    return O
+
+
+def hybrid_attn_noalloc(q, k, v, beta, gate, precision=None, out=None):
+    """hybrid_attn with the library's built-in scratch instead of a workspace: the
+    call allocates nothing on the device beyond `out` (pass it to allocate
+    nothing at all).  Shapes needing more than NOALLOC_SCRATCH_BYTES of workspace
+    raise; concurrent calls on one GPU race (they share its scratch)."""
+    torch = _torch()
+    prec = _precision_of(q, precision)
+    F, N, H, d = q.shape
+    dt = _io_dtype(prec)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _check_io(name, x, dt, (F, N, H, d))
+    _check_io("beta", beta, torch.float32, (F, H))
+    _check_io("gate", gate, torch.float32, (H, d))
+    O = torch.empty_like(q) if out is None else out
+    _check_io("out", O, dt, (F, N, H, d))
+    _check_no_alias("out", O, q=q, k=k, v=v, beta=beta, gate=gate)
+    st = load().vdn_hybrid_attn_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+                                        gate.data_ptr(), F, N, H, d, prec, O.data_ptr(), _stream())
+    _check(st, "vdn_hybrid_attn_noalloc")
     return O
 
 

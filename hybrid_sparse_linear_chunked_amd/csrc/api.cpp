@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <vector>
 
@@ -199,6 +200,7 @@ const char* vdn_status_string(int status) {
     case VDN_ERR_UNSUPPORTED: return "unsupported shape or precision";
     case VDN_ERR_WORKSPACE: return "workspace too small";
     case VDN_ERR_HIP: return "HIP error";
+    case VDN_ERR_TOO_LARGE: return "shape needs more scratch than vdn_hybrid_attn_noalloc holds";
   }
   return "unknown status";
 }
@@ -282,6 +284,56 @@ int vdn_hybrid_attn(const void* q, const void* k, const void* v, const float* be
   if (!bf16)
     VDN_STAGE(VDN_STAGE_READOUT, st, vdn::launch_readout(0, q, ws.at<void>(L.W), F, N, H, d, O, 1, st));
   return VDN_OK;
+}
+
+// ---- the layer without any allocation: workspace in a static device array
+}  // extern "C"
+
+namespace {
+
+// Workspace of vdn_hybrid_attn_noalloc.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address on each GPU comes from
+// hipGetSymbolAddress (each device holds its own copy), kept per device below and
+// used for every kernel argument.
+__device__ __align__(256) unsigned char scratch[VDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up once per device).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vdn_hybrid_attn_noalloc(const void* q, const void* k, const void* v, const float* beta, const float* gate,
+                            int F, int N, int H, int d, int precision, void* O, void* stream) {
+  int s = check_shape(F, N, H, d, precision);
+  if (s != VDN_OK) return s;
+  if (!q || !k || !v || !beta || !gate || !O) return VDN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(O, 16)) return VDN_ERR_INVALID_ARG;
+  const size_t need = layout(F, N, H, d, precision).total;
+  if (need > VDN_NOALLOC_SCRATCH_BYTES) return VDN_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  VDN_TRY(scratch_address(&ws));
+  // every piece of the workspace is written before it is read within one call
+  // (the fp8 maxima are cleared by a fill kernel), so nothing is cleared here
+  return vdn_hybrid_attn(q, k, v, beta, gate, F, N, H, d, precision, O, ws, VDN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ---- the layer followed by the two branches' output projections

@@ -59,6 +59,8 @@ extern "C" {
 #define VDN_ERR_UNSUPPORTED  (-2)  /* valid but unsupported (d, precision) combination   */
 #define VDN_ERR_WORKSPACE    (-3)  /* workspace smaller than vdn_workspace_bytes()      */
 #define VDN_ERR_HIP          (-4)  /* a HIP call failed; see vdn_last_hip_error()       */
+#define VDN_ERR_TOO_LARGE    (-5)  /* the shape needs more scratch than the built-in
+                                      array of vdn_hybrid_attn_noalloc holds            */
 
 /* Precisions. */
 #define VDN_PREC_FP32        0     /* q, k, v, O fp32; fp32 arithmetic                      */
@@ -82,6 +84,23 @@ int vdn_hybrid_attn(const void* q, const void* k, const void* v,
                     const float* beta, const float* gate,
                     int F, int N, int H, int d, int precision,
                     void* O, void* workspace, size_t workspace_bytes, void* stream);
+
+/* vdn_hybrid_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and the same result, bit for bit, with the workspace taken from a
+ * static device array of VDN_NOALLOC_SCRATCH_BYTES bytes that the library holds
+ * on every GPU it runs on until the process ends.  The call itself allocates and
+ * frees nothing.  Shapes whose vdn_workspace_bytes exceeds the array return
+ * VDN_ERR_TOO_LARGE before any device work (the 256-token, 30-frame, 8-head,
+ * d = 64 workload fits, in bf16 and fp8 q.k).  Every call on one GPU shares that
+ * GPU's array, which keeps the last call's contents: calls that overlap on one
+ * GPU (several streams or threads) race and must be serialised by the caller.
+ * Arguments and the other errors as in vdn_hybrid_attn. */
+#define VDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int vdn_hybrid_attn_noalloc(const void* q, const void* k, const void* v,
+                            const float* beta, const float* gate,
+                            int F, int N, int H, int d, int precision,
+                            void* O, void* stream);
 
 /* The layer with T extra (text or audio) tokens in the same sequence (arXiv
  * abstract page, Abstract; ananclaw note "Video DeltaNet ... critical read",

@@ -78,7 +78,7 @@ def test_workspace_bytes_rejects_bad_shapes(lib):
 
 
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4):
+    for s in (0, -1, -2, -3, -4, -5):
         assert lib.vdn_status_string(s)
     assert lib.vdn_last_hip_error() == 0
 
@@ -143,4 +143,18 @@ def test_mixed_and_projection_argument_errors(lib):
     assert gemm(A, A, 0, 128, 64, A, None) == vdn.ERR_INVALID_ARG
     assert gemm(None, A, 100, 128, 64, A, None) == vdn.ERR_INVALID_ARG
     assert gemm(A, A, 100, 128, 64, A + 4, None) == vdn.ERR_INVALID_ARG
+    assert lib.vdn_last_hip_error() == 0
+
+
+def test_noalloc_rejects_before_device_work(lib):
+    # argument and size checks of the no-allocation entry point come before any
+    # device work: too large a workspace, bad pointers and shapes return statuses
+    call = lib.vdn_hybrid_attn_noalloc
+    assert lib.vdn_workspace_bytes(45, 1024, 16, 128, 1) > vdn.NOALLOC_SCRATCH_BYTES
+    assert lib.vdn_workspace_bytes(30, 256, 8, 64, 2) <= vdn.NOALLOC_SCRATCH_BYTES
+    assert call(A, A, A, A, A, 45, 1024, 16, 128, 1, A, None) == vdn.ERR_TOO_LARGE
+    assert call(A, A, A, A, A, 90, 4032, 24, 128, 2, A, None) == vdn.ERR_TOO_LARGE
+    assert call(None, A, A, A, A, 20, 16, 2, 32, 0, A, None) == vdn.ERR_INVALID_ARG
+    assert call(A, A, A, A, A, 20, 16, 2, 48, 1, A, None) == vdn.ERR_UNSUPPORTED
+    assert call(A, A, A, A, A, 20, 16, 2, 32, 1, A + 8, None) == vdn.ERR_INVALID_ARG
     assert lib.vdn_last_hip_error() == 0
