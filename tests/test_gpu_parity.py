@@ -223,6 +223,24 @@ def test_fused_softmax_half_mid(precision):
     _fused_softmax_half(inp, precision, list(range(F)), list(range(H)), None)
 
 
+@pytest.mark.parametrize("precision", ["bf16", "bf16_fp8qk"])
+def test_w64_kernel_opt_in(precision, monkeypatch):
+    # the opt-in 64-queries-per-wave attention kernel (VDN_ATTN_W64=1): a ragged
+    # shape against the oracle in full, and the fused softmax half at N = 1024
+    monkeypatch.setenv("VDN_ATTN_W64", "1")
+    fp8 = precision == "bf16_fp8qk"
+    F, N, H, d = 24, 50, 2, 128
+    say(f"case w64 F={F} N={N} H={H} d={d} {precision}")
+    inp = Inputs(F, N, H, d, precision, seed=1)
+    got = run_all(inp, precision)
+    ref = oracle_slices(inp, list(range(F)), list(range(H)), fp8=fp8)
+    compare_full(inp, got, ref, "bf16")
+    F, N, H, d = 25, 1024, 3, 128
+    say(f"case w64 fused epilogue F={F} N={N} H={H} d={d} {precision}")
+    inp = Inputs(F, N, H, d, precision, seed=11)
+    _fused_softmax_half(inp, precision, list(range(F)), list(range(H)), None)
+
+
 def test_determinism():
     F, N, H, d = 30, 256, 4, 64
     inp = Inputs(F, N, H, d, "bf16", seed=5)
