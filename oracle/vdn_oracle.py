@@ -40,10 +40,14 @@ design notes): initial state zero; forward scan starts at frame 1 and the
 backward scan at frame F-2 (anchors excluded); the same beta in both directions;
 edge chunks see only the chunks that exist (no inward shift); softmax scale
 1/sqrt(d); anchor query frames have no linear output; additive merge with a
-per-(head, channel) gate; no normaliser in the linear readout.
+per-(head, channel) gate; no normaliser in the linear readout; the fp8 variant's
+quantiser (OCP E4M3, one power-of-two scale per head, q multiplied by the base-2
+softmax temperature before quantisation: fp8_qk_operands).
 
 Parity unpinned: that the VDA algebra above is the authors' update (the pages do
-not give it), and the fp8 (e4m3) softmax variant beyond the quantiser itself.
+not give it), and that the fp8 (e4m3) variant is the authors' (the pages name FP8
+without its format or scaling); the quantiser and operands are pinned against
+their own definition only.
 """
 from __future__ import annotations
 
@@ -425,19 +429,65 @@ def e4m3_round(x) -> np.ndarray:
 
 
 def fp8_head_scales(x) -> np.ndarray:
-    """Per-head amax of x [F, N, H, d] over all tokens and channels, float32 [H]."""
+    """Per-head amax of x [..., H, d] (head axis -2) over all tokens and channels,
+    float32 [H]."""
     x = np.asarray(x, dtype=np.float32)
-    return np.max(np.abs(x), axis=(0, 1, 3)).astype(np.float32)
+    axes = tuple(a for a in range(x.ndim) if a != x.ndim - 2)
+    return np.max(np.abs(x), axis=axes).astype(np.float32)
 
 
-def fp8_quantize(x, amax) -> np.ndarray:
-    """E4M3 codes (as float64 values) of x [F, N, H, d] with per-head amax [H]:
-    code = e4m3_round(fp32(x * fp32(448 / amax))).  The scale computation and the
-    product are float32 operations so the rounding decision is taken in the same
-    precision as the device."""
+def fp8_scale_exponent(amax) -> np.ndarray:
+    """Power-of-two quantiser scale per head: the smallest integer e with
+    amax <= 448 * 2^e, clamped to [-127, 127] (0 where amax is 0), int64 [H].
+    Found from the binary exponent of amax (exact; no logarithm is rounded)."""
+    out = []
+    for a in np.asarray(amax, dtype=np.float64).ravel():
+        if not a > 0:
+            out.append(0)
+            continue
+        e = -200
+        while not a <= E4M3_MAX * 2.0 ** e:      # 448 * 2^e is exact in float64
+            e += 1
+        out.append(min(max(e, -127), 127))
+    return np.asarray(out, dtype=np.int64)
+
+
+def fp8_quantize(x, e) -> np.ndarray:
+    """E4M3 codes (as float64 values) of x [..., H, d] with per-head power-of-two
+    scales 2^e [H]: code = e4m3_round(fp32(x * 2^-e)).  The product is a float32
+    operation (exact unless it falls below the float32 normal range), so the
+    rounding decision is taken in the same precision as the device."""
     x = np.asarray(x, dtype=np.float32)
-    amax = np.asarray(amax, dtype=np.float32)
-    inv = np.where(amax > 0, np.float32(E4M3_MAX) / np.where(amax > 0, amax, np.float32(1)),
-                   np.float32(0)).astype(np.float32)
-    scaled = (x * inv[None, None, :, None]).astype(np.float32)
+    inv = np.exp2(-np.asarray(e, dtype=np.float64)).astype(np.float32)
+    scaled = (x * inv.reshape((-1, 1))).astype(np.float32)
     return e4m3_round(scaled)
+
+
+def fp8_temperature(d: int) -> np.float32:
+    """The softmax temperature in base-2 units, log2(e) / sqrt(d), as the float32
+    value fp32(fp32(log2 e) / fp32(sqrt d))."""
+    return np.float32(np.float32(math.log2(math.e)) / np.sqrt(np.float32(d)))
+
+
+def fp8_qk_operands(q, k, d: int):
+    """(q_eff, k_eff), float64, such that the plain softmax branch on q_eff, k_eff
+    is the fp8 (E4M3) Q.K^T variant of the layer.
+
+    Reading (the pages name FP8 inference without giving its quantiser): q is
+    first multiplied by the base-2 temperature c = fp8_temperature(d) (float32),
+    then each of q' = fp32(q c) and k is quantised per head to E4M3 with the
+    power-of-two scale 2^e of fp8_scale_exponent over all of its tokens.  A score
+    in base-2 units is then 2^(e_q + e_k) * sum(code_q * code_k), and the
+    probabilities are 2^(that score - its row max).  In the units of the plain
+    branch (natural exponent of q.k / sqrt(d)) that is q_eff = code_q 2^e_q
+    sqrt(d) ln 2 and k_eff = code_k 2^e_k.  q, k: [..., H, d] (head axis -2)."""
+    c = fp8_temperature(d)
+    qp = (np.asarray(q, dtype=np.float32) * c).astype(np.float32)
+    kf = np.asarray(k, dtype=np.float32)
+    eq = fp8_scale_exponent(fp8_head_scales(qp))
+    ek = fp8_scale_exponent(fp8_head_scales(kf))
+    sq = np.exp2(eq.astype(np.float64)) * math.sqrt(d) * math.log(2.0)
+    sk = np.exp2(ek.astype(np.float64))
+    q_eff = fp8_quantize(qp, eq) * sq.reshape((-1, 1))
+    k_eff = fp8_quantize(kf, ek) * sk.reshape((-1, 1))
+    return q_eff, k_eff

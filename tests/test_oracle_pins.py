@@ -420,12 +420,62 @@ def test_e4m3_round_matches_torch_float8():
     np.testing.assert_array_equal(orc.e4m3_round(x), ref)
 
 
-def test_fp8_quantize_codes_in_range_and_amax_maps_to_max():
+def test_fp8_scale_exponent_is_the_smallest_power_of_two():
+    # hand-worked values: 448 * 2^e is the first bound at or above amax
+    f32 = np.float32
+    table = [(448.0, 0), (float(np.nextafter(f32(448.0), f32(1e9))), 1), (224.0, -1),
+             (float(np.nextafter(f32(224.0), f32(1e9))), 0), (1.0, -8), (1.75, -8), (1.7500001, -7),
+             (0.0, 0), (3.0e38, 120), (1e-44, -127), (448.0 * 2.0 ** 100, 100)]
+    got = orc.fp8_scale_exponent(np.array([a for a, _ in table], dtype=np.float32))
+    assert got.tolist() == [e for _, e in table]
+    # and the defining property over a wide random range
+    rng = np.random.default_rng(3)
+    a = (10.0 ** rng.uniform(-30, 30, 5000)).astype(np.float32).astype(np.float64)
+    e = orc.fp8_scale_exponent(a.astype(np.float32)).astype(np.float64)
+    assert np.all(a <= 448.0 * np.exp2(e))
+    assert np.all(a > 448.0 * np.exp2(e - 1))
+
+
+def test_fp8_quantize_power_of_two_codes():
+    # codes of x / 2^e: every head reaches (224, 448], and code * 2^e is within half
+    # an E4M3 step of x (relative 2^-4 in the normal range, 2^-10 * 2^e below it)
     F, N, H, d = 10, 8, 3, 16
     q, _, _ = small_inputs(F, N, H, d)
-    x = q.astype(np.float32)
-    amax = orc.fp8_head_scales(x)
-    codes = orc.fp8_quantize(x, amax)
-    assert np.abs(codes).max() <= 448.0
+    x = (q * np.array([1e-3, 1.0, 5e3])[None, None, :, None]).astype(np.float32)
+    e = orc.fp8_scale_exponent(orc.fp8_head_scales(x))
+    codes = orc.fp8_quantize(x, e)
+    back = codes * np.exp2(e.astype(np.float64))[:, None]
     for h in range(H):
-        assert np.abs(codes[:, :, h]).max() == 448.0
+        m = np.abs(codes[:, :, h]).max()
+        assert 224.0 < m <= 448.0
+    xs = x.astype(np.float64)
+    step = np.maximum(2.0 ** -4 * np.abs(xs), 2.0 ** -10 * np.exp2(e.astype(np.float64))[:, None])
+    assert np.all(np.abs(back - xs) <= step * (1 + 1e-12))
+
+
+def test_fp8_temperature_and_operands():
+    d = 128
+    c = orc.fp8_temperature(d)
+    assert c.dtype == np.float32
+    assert abs(float(c) - math.log2(math.e) / math.sqrt(d)) <= 2.0 ** -23 * float(c)
+    F, N, H = 6, 10, 2
+    rng = np.random.default_rng(4)
+    # k on the E4M3 grid times 2^5 with a head maximum of exactly 448 * 2^5: exact
+    grid = orc.e4m3_round(rng.uniform(-448, 448, (F, N, H, d)))
+    grid[0, 0, :, 0] = 448.0
+    k = grid * 32.0
+    q = rng.standard_normal((F, N, H, d)) * np.array([0.02, 30.0])[None, None, :, None]
+    q = q.astype(np.float32).astype(np.float64)
+    q_eff, k_eff = orc.fp8_qk_operands(q, k, d)
+    np.testing.assert_array_equal(k_eff, k)
+    # q_eff stands for q in the units of the plain branch: within half an E4M3 step
+    # of q (the temperature is divided out again, up to its float32 rounding)
+    eq = orc.fp8_scale_exponent(orc.fp8_head_scales((q.astype(np.float32) * c).astype(np.float32)))
+    unit = np.exp2(eq.astype(np.float64)) / float(c)        # value of one code unit, in q units
+    step = np.maximum(2.0 ** -4 * np.abs(q), 2.0 ** -10 * unit[:, None])
+    assert np.all(np.abs(q_eff - q) <= step * (1 + 1e-5) + 1e-6 * np.abs(q))
+    # and the scores: the plain softmax on (q_eff, k_eff) sees q.k within the same bound
+    s_eff = np.einsum("fnhd,gmhd->hfngm", q_eff, k_eff)
+    s_ref = np.einsum("fnhd,gmhd->hfngm", q, k)
+    bound = np.einsum("fnhd,gmhd->hfngm", np.abs(q) * 2.0 ** -4 + 2.0 ** -10 * unit[None, None, :, None], np.abs(k))
+    assert np.all(np.abs(s_eff - s_ref) <= bound * (1 + 1e-5) + 1e-9)
