@@ -40,7 +40,7 @@ _SIGS = {
     "vdn_softmax_branch": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "vdn_vda_states": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "vdn_vda_linear": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
-    "vdn_fp8_quantize": (_I, [_P, _I, _I, _I, _I, _P, _P, _P]),
+    "vdn_fp8_quantize": (_I, [_P, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P]),
     "vdn_schedule": (_I, [_I, ctypes.POINTER(ctypes.c_int), _I]),
     "vdn_set_stage_events": (_I, [_I, _P, _P]),
     "vdn_status_string": (ctypes.c_char_p, [_I]),
@@ -363,16 +363,18 @@ def vda_linear(q, S_fwd, S_bwd, precision=None, workspace=None):
     return O
 
 
-def fp8_quantize(x):
-    """(codes uint8 [F, N, H, d], amax fp32 [H]) of a bf16 tensor."""
+def fp8_quantize(x, prescale=1.0):
+    """(codes uint8 [F, N, H, d], scale_exp int32 [H]) of a bf16 tensor: E4M3 codes
+    of fp32(x * prescale) with per-head power-of-two scales 2^scale_exp."""
     torch = _torch()
     F, N, H, d = x.shape
     _check_io("x", x, torch.bfloat16)
     codes = torch.empty((F, N, H, d), dtype=torch.uint8, device=x.device)
-    amax = torch.empty((H,), dtype=torch.float32, device=x.device)
-    st = load().vdn_fp8_quantize(x.data_ptr(), F, N, H, d, codes.data_ptr(), amax.data_ptr(), _stream())
+    sexp = torch.empty((H,), dtype=torch.int32, device=x.device)
+    st = load().vdn_fp8_quantize(x.data_ptr(), F, N, H, d, float(prescale), codes.data_ptr(), sexp.data_ptr(),
+                                 _stream())
     _check(st, "vdn_fp8_quantize")
-    return codes, amax
+    return codes, sexp
 
 
 def set_stage_events(stage: int, before=None, after=None):

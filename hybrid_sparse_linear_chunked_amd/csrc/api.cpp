@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdint>
 #include <vector>
 
@@ -66,7 +67,7 @@ int check_extra(int F, int N, int T, int prec) {
 
 // Workspace carving (byte offsets).
 struct Layout {
-  size_t vt = 0, vtx = 0, px = 0, G = 0, B = 0, Sf = 0, Sb = 0, W = 0, pO = 0, pml = 0, q8 = 0, k8 = 0, amax = 0;
+  size_t vt = 0, vtx = 0, px = 0, G = 0, B = 0, Sf = 0, Sb = 0, W = 0, pO = 0, pml = 0, q8 = 0, k8 = 0, fexp = 0;
   size_t total = 0;
 };
 
@@ -101,7 +102,7 @@ Layout layout(int F, int N, int H, int d, int prec, int T = 0) {
     const size_t ntok = static_cast<size_t>(F) * N + T;
     L.q8 = take(ntok * H * d);
     L.k8 = take(ntok * H * d);
-    L.amax = take(2 * static_cast<size_t>(H) * 4);
+    L.fexp = take(2 * static_cast<size_t>(H) * 4);
   }
   L.total = off;
   return L;
@@ -133,20 +134,21 @@ int run_softmax(const void* q, const void* k, const void* v, int F, int N, int H
                 int T = 0, int split = 0) {
   const uint8_t* q8 = nullptr;
   const uint8_t* k8 = nullptr;
-  const float* amax = nullptr;
+  const int* fexp = nullptr;
   if (prec == VDN_PREC_BF16_FP8QK) {
-    // per-head scales over every token of the layer (the quantiser sees F*N+T
-    // tokens as one frame)
+    // per-head power-of-two scales over every token of the layer (the quantiser
+    // sees F*N+T tokens as one frame); q is quantised after its multiplication by
+    // the base-2 softmax temperature, so the Q.K^T MFMAs deliver log2 units
     const int qF = T > 0 ? 1 : F, qN = T > 0 ? F * N + T : N;
     VDN_TRY(mark(VDN_STAGE_QUANT, 0, st));
-    VDN_TRY(vdn::launch_fp8_quant(static_cast<const uint16_t*>(q), qF, qN, H, d, ws.at<uint8_t>(L.q8),
-                                  ws.at<float>(L.amax), st));
-    VDN_TRY(vdn::launch_fp8_quant(static_cast<const uint16_t*>(k), qF, qN, H, d, ws.at<uint8_t>(L.k8),
-                                  ws.at<float>(L.amax) + H, st));
+    VDN_TRY(vdn::launch_fp8_quant(static_cast<const uint16_t*>(q), qF, qN, H, d, vdn::softmax_temperature_log2(d),
+                                  ws.at<uint8_t>(L.q8), ws.at<int>(L.fexp), st));
+    VDN_TRY(vdn::launch_fp8_quant(static_cast<const uint16_t*>(k), qF, qN, H, d, 1.f, ws.at<uint8_t>(L.k8),
+                                  ws.at<int>(L.fexp) + H, st));
     VDN_TRY(mark(VDN_STAGE_QUANT, 1, st));
     q8 = ws.at<uint8_t>(L.q8);
     k8 = ws.at<uint8_t>(L.k8);
-    amax = ws.at<float>(L.amax);
+    fexp = ws.at<int>(L.fexp);
   }
   if (prec != VDN_PREC_FP32 && !vt_ready)
     VDN_STAGE(VDN_STAGE_PREP, st,
@@ -161,7 +163,7 @@ int run_softmax(const void* q, const void* k, const void* v, int F, int N, int H
   }
   const int kprec = prec == VDN_PREC_FP32 ? 0 : (prec == VDN_PREC_BF16 ? 1 : 2);
   VDN_STAGE(VDN_STAGE_ATTN, st,
-            vdn::launch_attn(kprec, q, k, v, ws.at<uint16_t>(L.vt), q8, k8, amax, F, N, H, d, O,
+            vdn::launch_attn(kprec, q, k, v, ws.at<uint16_t>(L.vt), q8, k8, fexp, F, N, H, d, O,
                              ws.at<float>(L.pO), ws.at<float>(L.pml), W, T, ws.at<uint16_t>(L.vtx), split,
                              ws.at<float>(L.px), st));
   VDN_STAGE(VDN_STAGE_COMBINE, st,
@@ -468,13 +470,15 @@ int vdn_vda_linear(const void* q, const float* S_fwd, const float* S_bwd, int F,
   return VDN_OK;
 }
 
-int vdn_fp8_quantize(const void* x, int F, int N, int H, int d, unsigned char* codes, float* amax,
-                     void* stream) {
+int vdn_fp8_quantize(const void* x, int F, int N, int H, int d, float prescale, unsigned char* codes,
+                     int* scale_exp, void* stream) {
   int s = check_shape(F, N, H, d, VDN_PREC_BF16_FP8QK);
   if (s != VDN_OK) return s;
-  if (!x || !codes || !amax) return VDN_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(amax, 4)) return VDN_ERR_INVALID_ARG;
-  VDN_TRY(vdn::launch_fp8_quant(static_cast<const uint16_t*>(x), F, N, H, d, codes, amax, as_stream(stream)));
+  if (!x || !codes || !scale_exp) return VDN_ERR_INVALID_ARG;
+  if (!(prescale > 0.f) || !std::isfinite(prescale)) return VDN_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(scale_exp, 4)) return VDN_ERR_INVALID_ARG;
+  VDN_TRY(vdn::launch_fp8_quant(static_cast<const uint16_t*>(x), F, N, H, d, prescale, codes, scale_exp,
+                                as_stream(stream)));
   return VDN_OK;
 }
 

@@ -16,7 +16,8 @@
 //                    query frames), K / V^T tiles double-buffered in LDS, online
 //                    softmax in fp32 registers, 32x32 MFMA for Q.K^T and P.V.
 //   combine_kernel   log-sum-exp merge of the anchor rows' key slices.
-//   amax / quant     per-head E4M3 quantiser of the fp8 Q.K^T variant.
+//   amax / fp8_exp / quant   per-head E4M3 quantiser (power-of-two scales) of
+//                    the fp8 Q.K^T variant.
 #include <type_traits>
 
 #include "attn_common.h"
@@ -274,8 +275,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     for (int s = 0; s < Cfg::QSTEPS; ++s)
       qb[s] = qvalid ? *reinterpret_cast<const bf16x8*>(q + qoff + 16 * s + 8 * hf) : bf16x8{};
   }
-  float scale = a.scale_log2;
-  if constexpr (FP8) scale *= (a.amax[h] * (1.f / 448.f)) * (a.amax[H + h] * (1.f / 448.f));
+  // fp8: the q codes carry the base-2 temperature, a score is 2^(e_q + e_k) times
+  // the code products
+  const float scale = FP8 ? __builtin_ldexpf(1.f, a.fexp[h] + a.fexp[H + h]) : a.scale_log2;
 
   // ---------------- tile loader
   auto tile_frame = [&](int t, int& f, int& b) {
@@ -404,7 +406,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
           const uint4* p = reinterpret_cast<const uint4*>(base + krow * Cfg::KP + 64 * st + 32 * hf);
           uint4 x0 = p[0], x1 = p[1];
           intx8 ka = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-          s[kb] = mfma_fp8(ka, q8f[st], s[kb]);
+          s[kb] = mfma_fp8_scaled(ka, q8f[st], s[kb], 127, 127);   // (scales applied in the exponent)
         }
       } else {
         const uint16_t* Ks = reinterpret_cast<const uint16_t*>(base);
@@ -599,9 +601,8 @@ __device__ inline Item decode_item_x(const AttnArgs& a, int* xslot) {
 // SPLIT: chunk items write O_soft and g (.) O_lin side by side (token stride 2 H D,
 // the output projection's input) instead of their sum.
 template <int D, int PREC, int NW, bool XT, bool SPLIT, bool XI = false>
-// (waves per SIMD: 2 at d = 128, which needs ~240 registers; the fp8 path at d = 64
-// fits 128 registers, i.e. two workgroups per CU)
-__global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_lds_kernel(AttnArgs a) {
+// (two waves per SIMD: d = 128 needs ~240 registers)
+__global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   using Cfg = LdsCfg<D, PREC>;
   constexpr bool FP8 = Cfg::FP8;
   constexpr int NDB = D / 32;
@@ -649,11 +650,16 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
     for (int s = 0; s < Cfg::QSTEPS; ++s)
       qb[s] = qvalid ? *reinterpret_cast<const bf16x8*>(q + qoff + 16 * s + 8 * hf) : bf16x8{};
   }
-  float scale = a.scale_log2;
-  if constexpr (FP8) scale *= (a.amax[h] * (1.f / 448.f)) * (a.amax[H + h] * (1.f / 448.f));
-  if constexpr (!FP8) {
-    // bf16: the Q operand carries the factor log2(e)/sqrt(d) (rounded once to
-    // bf16), so the MFMAs deliver scores in log2 units directly
+  // The MFMAs deliver scores in log2 units directly.  bf16: the Q operand carries
+  // the factor log2(e)/sqrt(d) (rounded once to bf16).  fp8: the q codes carry it
+  // (applied before quantisation), and the power-of-two scales of the q and k
+  // codes are the MFMA's E8M0 operand scales (sq for Q, sk for K)
+  int sq = 0, sk = 0;
+  if constexpr (FP8) {
+    sq = a.fexp[h] + 127;
+    sk = a.fexp[H + h] + 127;
+  } else {
+    const float scale = a.scale_log2;
 #pragma unroll
     for (int s = 0; s < Cfg::QSTEPS; ++s)
 #pragma unroll
@@ -736,10 +742,10 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
   floatx16 o[NDB];
 #pragma unroll
   for (int x = 0; x < NDB; ++x) o[x] = floatx16{};
-  // running max m (log2 units).  bf16: the Q.K^T accumulators start at -m, so
-  // the MFMAs leave s - m and the exponent needs no VALU op; m is finite from the
+  // running max m (log2 units).  The Q.K^T accumulators start at -m, so the
+  // MFMAs leave s - m and the exponent needs no VALU op; m is finite from the
   // start and the first tile sets it to that tile's maximum
-  float m_run = FP8 ? -INFINITY : 0.f, l_run = 0.f;
+  float m_run = 0.f, l_run = 0.f;
   floatx16 nm = floatx16{};      // -m in every element: the first Q.K^T accumulator input
   if constexpr (XI) {
     // start from the state after the extra tokens' keys (l on the first half-wave
@@ -814,14 +820,7 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
     constexpr int NQK = 2 * Cfg::QSTEPS, QB = NQK < kQkBatch ? NQK : kQkBatch, NQB = NQK / QB;
     typename LdsCfg<D, PREC>::KFrag kf[2][QB];
     bf16x8 va[2][NDB];
-    floatx16 s[2];
-    if constexpr (FP8) {
-      s[0] = floatx16{};
-      s[1] = floatx16{};
-    } else {
-      s[0] = nm;
-      s[1] = nm;
-    }
+    floatx16 s[2] = {nm, nm};
 #pragma unroll
     for (int x = 0; x < QB; ++x) kf[0][x] = Cfg::kfrag(sbase, x, j, hf);
 #pragma unroll
@@ -842,7 +841,7 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
 #pragma unroll
       for (int x = 0; x < QB; ++x) {
         const int i = bt * QB + x, st = i >> 1, kb = i & 1;
-        if constexpr (FP8) s[kb] = mfma_fp8(kf[bt & 1][x], q8f[st], s[kb]);
+        if constexpr (FP8) s[kb] = mfma_fp8_scaled(kf[bt & 1][x], q8f[st], s[kb], sk, sq);
         else s[kb] = mfma_bf16(kf[bt & 1][x], qb[st], s[kb]);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -864,17 +863,7 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
     // (a row's maximum is split over the two lanes of a pair, both in this wave:
     // the wave-wide test gives the same answer on the per-lane parts, so the pair
     // combine runs only when the maximum is raised)
-    if constexpr (FP8) {
-      if (__any(mx * scale > m_run + kLazy)) {
-        const float mt = pair_max(mx) * scale;
-        const float m_new = __builtin_fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int x = 0; x < NDB; ++x) o[x] *= alpha;
-      }
-    } else {
+    {
       // scores are s - m already: raise m by the excess (on the first tile, by the
       // tile maximum whatever its sign; nothing is accumulated yet to rescale)
       const bool first = !XI && t == 0;     // nothing accumulated yet
@@ -897,11 +886,8 @@ __global__ __launch_bounds__(64 * NW, (PREC == 2 && D <= 64) ? 4 : 2) void attn_
       }
       asm volatile("" : "+v"(nm));   // keep it in registers rather than rebuild it every tile
     }
-    const float neg_m = -m_run;
-    // exponent of a score: bf16 scores are already s - m in log2 units
-    auto expo = [&](float x) {
-      return FP8 ? __builtin_amdgcn_exp2f(fmaf(x, scale, neg_m)) : __builtin_amdgcn_exp2f(x);
-    };
+    // exponent of a score: the scores are already s - m in log2 units
+    auto expo = [&](float x) { return __builtin_amdgcn_exp2f(x); };
 
     // ---- O^T += V^T P^T, one group of 16 keys per batch; the probabilities of
     // the next group are formed on the VALU while this group's MFMAs run, and
@@ -1200,23 +1186,42 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
   }
 }
 
-// 8 elements per thread.
+// The power-of-two scale exponent of a head: the smallest integer e with
+// amax <= 448 * 2^e, clamped to [-127, 127] (an E8M0 scale byte is e + 127); 0 for
+// amax = 0.  From the binary exponent of amax: amax = f 2^x with f in [0.5, 1),
+// and 448 = 0.875 * 2^9, so e = x - 9 if f <= 0.875, else x - 8 (exact).
+__device__ inline int fp8_scale_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const int x = __builtin_amdgcn_frexp_expf(amax);
+  const float f = __builtin_amdgcn_frexp_mantf(amax);
+  const int e = f <= 0.875f ? x - 9 : x - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// one thread per head: amax bits (from amax_kernel) -> scale exponent, in place;
+// the amax is that of fp32(x * prescale)
+__global__ void fp8_exp_kernel(uint32_t* __restrict__ bits, int H, float prescale) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h < H) bits[h] = static_cast<uint32_t>(fp8_scale_exponent(__uint_as_float(bits[h]) * prescale));
+}
+
+// 8 elements per thread: code = E4M3(fp32(fp32(x * prescale) * 2^-e[h]))
 template <int D>
 __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__ x, size_t n8, int H,
-                                                    const float* __restrict__ amax,
+                                                    const int* __restrict__ fexp, float prescale,
                                                     uint8_t* __restrict__ codes) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n8) return;
   const int h = static_cast<int>((i / (D / 8)) % H);
-  const float am = amax[h];
-  const float inv = am > 0.f ? 448.f / am : 0.f;
+  const int ne = -fexp[h];
   const uint4 val = *reinterpret_cast<const uint4*>(x + 8 * i);
   const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
   uint32_t out[2] = {0, 0};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t bits = (e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16);
-    const uint32_t c = f32_to_e4m3(__uint_as_float(bits) * inv);
+    const float y = __uint_as_float(bits) * prescale;               // one fp32 rounding
+    const uint32_t c = f32_to_e4m3(__builtin_ldexpf(y, ne));         // exact scaling
     out[e >> 2] |= c << (8 * (e & 3));
   }
   *reinterpret_cast<uint2*>(codes + 8 * i) = make_uint2(out[0], out[1]);
@@ -1294,11 +1299,11 @@ static hipError_t attn_lds(const AttnArgs& a, hipStream_t st, bool split) {
 }
 
 hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, const uint16_t* vt,
-                       const uint8_t* q8, const uint8_t* k8, const float* amax, int F, int N, int H,
+                       const uint8_t* q8, const uint8_t* k8, const int* fexp, int F, int N, int H,
                        int D, void* O, float* part_O, float* part_ml, const uint16_t* W,
                        int T, const uint16_t* vtx, int split, float* px, hipStream_t st) {
   AttnArgs a;
-  a.q = q; a.k = k; a.v = v; a.vt = vt; a.q8 = q8; a.k8 = k8; a.amax = amax;
+  a.q = q; a.k = k; a.v = v; a.vt = vt; a.q8 = q8; a.k8 = k8; a.fexp = fexp;
   a.O = O; a.part_O = part_O; a.part_ml = part_ml;
   a.W = W;
   a.T = T;
@@ -1313,7 +1318,7 @@ hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, co
   a.F = F; a.N = N; a.H = H;
   attn_split_plan(F, &a.nsplit, &a.fs);
   a.na = F >= 2 ? 2 : 1;
-  a.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+  a.scale_log2 = softmax_temperature_log2(D);
   if (prec == 0) {
     if (D == 32) return attn_f32<32>(a, st);
     if (D == 64) return attn_f32<64>(a, st);
@@ -1353,22 +1358,24 @@ hipError_t launch_combine(int prec, const float* part_O, const float* part_ml, i
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fp8_quant(const uint16_t* x, int F, int N, int H, int D, uint8_t* codes,
-                            float* amax, hipStream_t st) {
+hipError_t launch_fp8_quant(const uint16_t* x, int F, int N, int H, int D, float prescale, uint8_t* codes,
+                            int* fexp, hipStream_t st) {
   const size_t ntok = (size_t)F * N;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((H + 255) / 256), dim3(256), 0, st,
-                     reinterpret_cast<uint32_t*>(amax), H, 0u);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(fexp);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((H + 255) / 256), dim3(256), 0, st, bits, H, 0u);
   const dim3 g1((unsigned)((ntok + 1023) / 1024), H);
   const size_t n8 = ntok * H * D / 8;
   const dim3 g2((unsigned)((n8 + 255) / 256));
   switch (D) {
     case 64:
-      hipLaunchKernelGGL(amax_kernel<64>, g1, dim3(256), 0, st, x, ntok, H, reinterpret_cast<uint32_t*>(amax));
-      hipLaunchKernelGGL(quant_kernel<64>, g2, dim3(256), 0, st, x, n8, H, amax, codes);
+      hipLaunchKernelGGL(amax_kernel<64>, g1, dim3(256), 0, st, x, ntok, H, bits);
+      hipLaunchKernelGGL(fp8_exp_kernel, dim3((H + 63) / 64), dim3(64), 0, st, bits, H, prescale);
+      hipLaunchKernelGGL(quant_kernel<64>, g2, dim3(256), 0, st, x, n8, H, fexp, prescale, codes);
       break;
     case 128:
-      hipLaunchKernelGGL(amax_kernel<128>, g1, dim3(256), 0, st, x, ntok, H, reinterpret_cast<uint32_t*>(amax));
-      hipLaunchKernelGGL(quant_kernel<128>, g2, dim3(256), 0, st, x, n8, H, amax, codes);
+      hipLaunchKernelGGL(amax_kernel<128>, g1, dim3(256), 0, st, x, ntok, H, bits);
+      hipLaunchKernelGGL(fp8_exp_kernel, dim3((H + 63) / 64), dim3(64), 0, st, bits, H, prescale);
+      hipLaunchKernelGGL(quant_kernel<128>, g2, dim3(256), 0, st, x, n8, H, fexp, prescale, codes);
       break;
     default:
       return hipErrorInvalidValue;

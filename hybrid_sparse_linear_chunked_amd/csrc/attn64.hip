@@ -24,7 +24,8 @@ namespace vdn {
 // inserted by hand (score_fence, acc_fence: 32 / 64 cycles, more than the 8-pass
 // bf16 and 16-pass fp8 MFMAs need); operands written by the VALU or by LDS reads
 // are produced well before their MFMA, behind explicit waits.
-// Score MFMAs S = K Q^T (+ c): the Q fragment qi (query block x, reduction step
+// Score MFMAs S = K Q^T (+ c) (fp8: each product scaled by the E8M0 bytes sk, sq):
+// the Q fragment qi (query block x, reduction step
 // st: qi = steps * x + st) is pinned to accumulation registers from a128 on, read
 // there as the B operand (an in-out operand of the asm, so that the value stays
 // in those registers between uses); the scores land in VGPRs.  FIRST starts from
@@ -32,17 +33,21 @@ namespace vdn {
 #define VDN_QK(T, QI, LO, HI)                                                                       \
   case QI:                                                                                           \
     if (FIRST)                                                                                       \
-      asm volatile("v_mfma_f32_32x32x" VDN_KSTR(T) " %0, %2, %1, %3"                                 \
+      asm volatile(VDN_QK_OP(T) " %0, %2, %1, %3" VDN_QK_SCALES(T)                                   \
                    : "=&v"(acc), "+{a[" #LO ":" #HI "]}"(q)                                          \
-                   : "v"(k), "v"(c));                                                                \
+                   : "v"(k), "v"(c), "v"(sk), "v"(sq));                                              \
     else                                                                                             \
-      asm volatile("v_mfma_f32_32x32x" VDN_KSTR(T) " %0, %2, %1, %0"                                 \
+      asm volatile(VDN_QK_OP(T) " %0, %2, %1, %0" VDN_QK_SCALES(T)                                   \
                    : "+v"(acc), "+{a[" #LO ":" #HI "]}"(q)                                           \
-                   : "v"(k));                                                                        \
+                   : "v"(k), "v"(c), "v"(sk), "v"(sq));                                              \
     break;
-#define VDN_KSTR(T) VDN_KSTR_##T
-#define VDN_KSTR_bf16 "16_bf16"
-#define VDN_KSTR_f8f6f4 "64_f8f6f4"
+#define VDN_QK_OP(T) VDN_QK_OP_##T
+#define VDN_QK_OP_bf16 "v_mfma_f32_32x32x16_bf16"
+#define VDN_QK_OP_f8f6f4 "v_mfma_scale_f32_32x32x64_f8f6f4"
+// fp8: E8M0 scale bytes of K (operand A) and Q (operand B), low byte of each register
+#define VDN_QK_SCALES(T) VDN_QK_SCALES_##T
+#define VDN_QK_SCALES_bf16 ""
+#define VDN_QK_SCALES_f8f6f4 ", %4, %5 op_sel_hi:[0,0,0]"
 template <bool FP8>
 struct Mma;
 template <>
@@ -51,7 +56,7 @@ struct Mma<false> {
   using QFrag = bf16x8;
   template <bool FIRST>
   __device__ __forceinline__ static void qk(int qi, floatx16& acc, const KFrag& k, QFrag& q,
-                                            const floatx16& c) {
+                                            const floatx16& c, int sk, int sq) {
     switch (qi) {
       VDN_QK(bf16, 0, 128, 131)
       VDN_QK(bf16, 1, 132, 135)
@@ -78,7 +83,7 @@ struct Mma<true> {
   using QFrag = intx8;
   template <bool FIRST>
   __device__ __forceinline__ static void qk(int qi, floatx16& acc, const KFrag& k, QFrag& q,
-                                            const floatx16& c) {
+                                            const floatx16& c, int sk, int sq) {
     switch (qi) {
       VDN_QK(f8f6f4, 0, 128, 135)
       VDN_QK(f8f6f4, 1, 136, 143)
@@ -88,6 +93,12 @@ struct Mma<true> {
   }
 };
 #undef VDN_QK
+#undef VDN_QK_OP
+#undef VDN_QK_OP_bf16
+#undef VDN_QK_OP_f8f6f4
+#undef VDN_QK_SCALES
+#undef VDN_QK_SCALES_bf16
+#undef VDN_QK_SCALES_f8f6f4
 // Places the Q fragments in their pinned registers with the wait states an MFMA
 // needs after they are written there (the copies happen before this statement)
 __device__ __forceinline__ void q_fence(bf16x8 (&q)[2][8]) {
@@ -254,8 +265,10 @@ __global__ __launch_bounds__(256, 1) void attn_w64_kernel(AttnArgs a) {
     }
   }
   q_fence(qf);
-  float scale = a.scale_log2;
-  if constexpr (FP8) scale *= (a.amax[h] * (1.f / 448.f)) * (a.amax[H + h] * (1.f / 448.f));
+  // fp8: the q codes carry log2(e)/sqrt(d); the power-of-two scales of the q and
+  // k codes are the score MFMAs' E8M0 operand scales, so every score arrives in
+  // log2 units, as at bf16
+  const int sq = FP8 ? a.fexp[h] + 127 : 0, sk = FP8 ? a.fexp[H + h] + 127 : 0;
 
   // ---- global -> LDS tile loads (the padded layout of attn_lds_kernel, four
   // waves).  Every wave issues the same number of loads per tile, with no branch:
@@ -335,7 +348,7 @@ __global__ __launch_bounds__(256, 1) void attn_w64_kernel(AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[x][db] = floatx16{};
   float m_run[NX], l_run[NX];         // running max (log2 units), per-lane row-sum part
-  // The score accumulators start at -m (fp8: -m / scale, in the MFMA's units), so
+  // The score accumulators start at -m, so
   // the MFMAs deliver scores already shifted by the running max
   floatx16 nm[NX];
 #pragma unroll
@@ -344,11 +357,10 @@ __global__ __launch_bounds__(256, 1) void attn_w64_kernel(AttnArgs a) {
     l_run[x] = 0.f;
     nm[x] = floatx16{};
   }
-  // a shifted score in log2 units (bf16: Q carries the scale; fp8: the score scale
-  // holds both quantiser scales and log2(e)/sqrt(d))
-  auto lg = [&](float s) { return FP8 ? s * scale : s; };
+  // a shifted score in log2 units (the MFMAs deliver log2 units at both precisions)
+  auto lg = [&](float s) { return s; };
   auto set_nm = [&](int x) {
-    const float v = FP8 ? -m_run[x] / scale : -m_run[x];
+    const float v = -m_run[x];
 #pragma unroll
     for (int r = 0; r < 16; ++r) nm[x][r] = v;
   };
@@ -393,7 +405,7 @@ __global__ __launch_bounds__(256, 1) void attn_w64_kernel(AttnArgs a) {
           resc = 1;
         }
         m_run[x] += dm;
-        const float ds = FP8 ? dm / scale : dm;
+        const float ds = dm;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[x][r] -= ds;
         set_nm(x);
@@ -438,8 +450,8 @@ __global__ __launch_bounds__(256, 1) void attn_w64_kernel(AttnArgs a) {
       const KFrag kf = Cfg::kfrag(smem, 2 * st, j, hf);
 #pragma unroll
       for (int x = 0; x < NX; ++x) {
-        if (st == 0) M::template qk<true>(QS * x + st, sn[x], kf, qf[x][st], nm[x]);
-        else M::template qk<false>(QS * x + st, sn[x], kf, qf[x][st], nm[x]);
+        if (st == 0) M::template qk<true>(QS * x + st, sn[x], kf, qf[x][st], nm[x], sk, sq);
+        else M::template qk<false>(QS * x + st, sn[x], kf, qf[x][st], nm[x], sk, sq);
       }
     }
     score_fence2(sn);
@@ -540,8 +552,8 @@ __global__ __launch_bounds__(256, 1) void attn_w64_kernel(AttnArgs a) {
         }
 #pragma unroll
         for (int x = 0; x < NX; ++x) {
-          if (st == 0) M::template qk<true>(QS * x + st, sn[x], kf, qf[x][st], nm[x]);
-          else M::template qk<false>(QS * x + st, sn[x], kf, qf[x][st], nm[x]);
+          if (st == 0) M::template qk<true>(QS * x + st, sn[x], kf, qf[x][st], nm[x], sk, sq);
+          else M::template qk<false>(QS * x + st, sn[x], kf, qf[x][st], nm[x], sk, sq);
         }
         __builtin_amdgcn_sched_barrier(0);
       }

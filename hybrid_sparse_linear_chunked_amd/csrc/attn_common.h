@@ -26,7 +26,7 @@ struct AttnArgs {
   const uint16_t* vt;     // bf16 / fp8 paths: transposed v
   const uint8_t* q8;      // fp8 path: E4M3 codes
   const uint8_t* k8;
-  const float* amax;      // fp8 path: [2][H] (q then k)
+  const int* fexp;        // fp8 path: [2][H] power-of-two scale exponents (q then k)
   void* O;
   float* part_O;          // [nsplit][H][na][N][D]
   float* part_ml;         // [nsplit][H][na][N][2]

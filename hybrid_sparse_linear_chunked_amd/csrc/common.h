@@ -81,9 +81,11 @@ __device__ inline floatx16 mfma_bf16(const bf16x8& a, const bf16x8& b, const flo
 __device__ inline floatx16 mfma_f32(float a, float b, const floatx16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
-// OCP E4M3 x E4M3, 64-deep reduction (32 codes per lane per operand).
-__device__ inline floatx16 mfma_fp8(const intx8& a, const intx8& b, const floatx16& c) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+// OCP E4M3 x E4M3, 64-deep reduction (32 codes per lane per operand), every
+// product scaled by 2^(sa - 127) 2^(sb - 127): sa, sb are E8M0 scale bytes (the
+// low byte of each register is used), applied exactly by the matrix core.
+__device__ inline floatx16 mfma_fp8_scaled(const intx8& a, const intx8& b, const floatx16& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
 // max / sum of x over the lane pair (j, j + 32), in both lanes: v_permlane32_swap

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <cmath>
 
 namespace vdn {
 
@@ -32,13 +33,16 @@ hipError_t launch_proj(const uint16_t* A, const uint16_t* B, int M, int N, int K
 hipError_t launch_prep(const uint16_t* k, const uint16_t* v, int F, int N, int H, int D,
                        uint16_t* vt, float* G, float* B, int grams, hipStream_t st);
 hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, const uint16_t* vt,
-                       const uint8_t* q8, const uint8_t* k8, const float* amax, int F, int N, int H,
+                       const uint8_t* q8, const uint8_t* k8, const int* fexp, int F, int N, int H,
                        int D, void* O, float* part_O, float* part_ml, const uint16_t* W,
                        int T, const uint16_t* vtx, int split, float* px, hipStream_t st);
 hipError_t launch_combine(int prec, const float* part_O, const float* part_ml, int F, int N, int T,
                           int H, int D, void* O, int split, hipStream_t st);
-hipError_t launch_fp8_quant(const uint16_t* x, int F, int N, int H, int D, uint8_t* codes,
-                            float* amax, hipStream_t st);
+// The softmax temperature in base-2 units, log2(e) / sqrt(d), in fp32 (the bf16
+// Q operand and the fp8 q codes carry it)
+inline float softmax_temperature_log2(int d) { return 1.4426950408889634f / sqrtf(static_cast<float>(d)); }
+hipError_t launch_fp8_quant(const uint16_t* x, int F, int N, int H, int D, float prescale, uint8_t* codes,
+                            int* fexp, hipStream_t st);
 void attn_split_plan(int F, int* nsplit, int* fs);
 
 // vda.hip

@@ -66,8 +66,9 @@ extern "C" {
 #define VDN_PREC_FP32        0     /* q, k, v, O fp32; fp32 arithmetic                      */
 #define VDN_PREC_BF16        1     /* q, k, v, O bf16; fp32 accumulation                    */
 #define VDN_PREC_BF16_FP8QK  2     /* bf16 I/O; the softmax branch's q.k products use OCP
-                                      E4M3 codes with per-head scales amax/448 computed
-                                      internally; P.V, the VDA branch and the merge as bf16 */
+                                      E4M3 codes with per-head power-of-two scales computed
+                                      internally (q first multiplied by log2(e)/sqrt(d));
+                                      P.V, the VDA branch and the merge as bf16 */
 
 /* Bytes of workspace the calls below need for this shape; 0 if the shape or
  * precision is invalid or unsupported. */
@@ -182,13 +183,20 @@ int vdn_vda_linear(const void* q, const float* S_fwd, const float* S_bwd,
  * Results: branch-specific Ulysses sequence parallelism and FP8; model card
  * "Video DeltaNet: Hybrid Attention to Speed Up Video Models with Near-Lossless
  * Quality", section Your first render: the 8nfe_tuned_fp8 configuration) without
- * naming the format or the scaling; this library takes OCP E4M3 with one scale per
- * head:
- * amax[h] = max |x| over head h (fp32), code = E4M3(RNE, saturating) of
- * fp32(x * fp32(448 / amax[h])) (0 where amax is 0).  x: bf16 [F, N, H, d];
- * codes: uint8 [F, N, H, d] (OCP E4M3 "FN" bit patterns); amax: fp32 [H]. */
-int vdn_fp8_quantize(const void* x, int F, int N, int H, int d,
-                     unsigned char* codes, float* amax, void* stream);
+ * naming the format or the scaling; this library takes OCP E4M3 with one
+ * power-of-two scale per head, so that the matrix core applies the scales exactly
+ * (E8M0 operand scales) and the scores need no rescaling on the vector units:
+ *   y = fp32(x * prescale);  amax[h] = max |y| over head h;
+ *   scale_exp[h] = the smallest integer e with amax[h] <= 448 * 2^e, clamped to
+ *                  [-127, 127] (0 where amax[h] is 0);
+ *   code = E4M3(RNE, saturating) of fp32(y * 2^-scale_exp[h]).
+ * The layer quantises q with prescale = fp32(log2(e) / sqrt(d)) (so that a score
+ * in base-2 units is 2^(e_q + e_k) times the code products) and k with 1.
+ * x: bf16 [F, N, H, d]; prescale: finite and > 0, else VDN_ERR_INVALID_ARG;
+ * codes: uint8 [F, N, H, d] (OCP E4M3 "FN" bit patterns); scale_exp: int32 [H],
+ * also used as scratch during the call.  d: 64 or 128. */
+int vdn_fp8_quantize(const void* x, int F, int N, int H, int d, float prescale,
+                     unsigned char* codes, int* scale_exp, void* stream);
 
 /* Frame partition of the layer for F frames (host only, no device work): the
  * softmax key frames of every query frame (sd114.wiki article, section

@@ -104,8 +104,10 @@ def test_argument_errors_return_before_launch(lib):
     assert lib.vdn_softmax_branch(A, A, A, F, N, H, d, 1, A, A, need - 1, None) == vdn.ERR_WORKSPACE
     assert lib.vdn_vda_states(A, A, None, F, N, H, d, 1, A, A, A, need, None) == vdn.ERR_INVALID_ARG
     assert lib.vdn_vda_linear(A, A, A, F, N, H, 64 + 1, 1, A, A, need, None) == vdn.ERR_UNSUPPORTED
-    assert lib.vdn_fp8_quantize(A, F, N, H, 32, A, A, None) == vdn.ERR_UNSUPPORTED
-    assert lib.vdn_fp8_quantize(None, F, N, H, 64, A, A, None) == vdn.ERR_INVALID_ARG
+    assert lib.vdn_fp8_quantize(A, F, N, H, 32, 1.0, A, A, None) == vdn.ERR_UNSUPPORTED
+    assert lib.vdn_fp8_quantize(None, F, N, H, 64, 1.0, A, A, None) == vdn.ERR_INVALID_ARG
+    assert lib.vdn_fp8_quantize(A, F, N, H, 64, 0.0, A, A, None) == vdn.ERR_INVALID_ARG
+    assert lib.vdn_fp8_quantize(A, F, N, H, 64, float("inf"), A, A, None) == vdn.ERR_INVALID_ARG
     assert lib.vdn_last_hip_error() == 0
 
 

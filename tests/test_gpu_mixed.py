@@ -67,8 +67,8 @@ class MixedInputs:
 
 def oracle_mixed(inp, frames, heads, tokens=None, xtokens=None, fp8=False):
     """Oracle (O_soft video, O video, O extra) on the sampled frames / tokens /
-    extra tokens / heads; with fp8=True the softmax sees the E4M3-quantised q, k
-    (per-head scale amax/448 over all F*N + T tokens)."""
+    extra tokens / heads; with fp8=True the softmax sees the oracle's fp8 q, k
+    operands (per-head power-of-two scales over all F*N + T tokens)."""
     q, qx = inp.host64("q", heads)
     k, kx = inp.host64("k", heads)
     v, vx = inp.host64("v", heads)
@@ -76,15 +76,12 @@ def oracle_mixed(inp, frames, heads, tokens=None, xtokens=None, fp8=False):
     gate = inp.gate.numpy().astype(np.float64)[heads]
     qs, ks, qxs, kxs = q, k, qx, kx
     if fp8:
-        def quant(a, ax):
-            allt = np.concatenate([a.reshape(-1, *a.shape[2:]), ax], axis=0)[None].astype(np.float32)
-            am = orc.fp8_head_scales(allt)
-            deq = orc.fp8_quantize(allt, am) * (am.astype(np.float64) / 448.0)[None, None, :, None]
-            deq = deq[0]
-            n = a.shape[0] * a.shape[1]
-            return deq[:n].reshape(a.shape), deq[n:]
-        qs, qxs = quant(q, qx)
-        ks, kxs = quant(k, kx)
+        n = q.shape[0] * q.shape[1]
+        allq = np.concatenate([q.reshape(-1, *q.shape[2:]), qx], axis=0)
+        allk = np.concatenate([k.reshape(-1, *k.shape[2:]), kx], axis=0)
+        qe, ke = orc.fp8_qk_operands(allq, allk, q.shape[-1])
+        qs, qxs = qe[:n].reshape(q.shape), qe[n:]
+        ks, kxs = ke[:n].reshape(k.shape), ke[n:]
     O_soft = orc.softmax_branch_mixed(qs, ks, v, kxs, vx, frames=frames, tokens=tokens)
     O_x = orc.softmax_extra_rows(ks, v, qxs, kxs, vx, xtokens=xtokens)
     Sf, Sb = orc.vda_states(k, v, beta)

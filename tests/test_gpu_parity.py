@@ -13,6 +13,7 @@ epilogue, and at these input distributions the gated linear term dominates O
 therefore isolated on its own: with g = 0 the layer must equal the softmax branch
 bit for bit, and with a small gate (so that O_soft carries most of |O|) the layer
 must match the oracle."""
+import math
 import os
 import sys
 
@@ -250,15 +251,22 @@ def test_determinism():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_fp8_codes_bit_exact():
+@pytest.mark.parametrize("magnitude, temperature", [(1.0, False), (1.0, True), (3e-30, False), (2e4, True)])
+def test_fp8_codes_bit_exact(magnitude, temperature):
+    # codes and power-of-two scale exponents bit for bit against the oracle's
+    # quantiser, with and without the base-2 temperature as prescale, at magnitudes
+    # that take the exponents far below and above zero
     F, N, H, d = 12, 333, 3, 128
     inp = Inputs(F, N, H, d, "bf16", seed=6)
-    codes, amax = vdn.fp8_quantize(inp.dq)
+    xb = (inp.q.to(torch.float32) * magnitude).to(torch.bfloat16)
+    pre = np.float32(np.float32(math.log2(math.e)) / np.sqrt(np.float32(d))) if temperature else np.float32(1.0)
+    codes, sexp = vdn.fp8_quantize(xb.to("cuda"), float(pre))
     torch.cuda.synchronize()
-    x = inp.q.to(torch.float32).numpy()
-    ram = orc.fp8_head_scales(x)
-    np.testing.assert_array_equal(amax.cpu().numpy(), ram)
-    ref = orc.fp8_quantize(x, ram)
+    y = (xb.to(torch.float32).numpy() * pre).astype(np.float32)
+    e = orc.fp8_scale_exponent(orc.fp8_head_scales(y))
+    say(f"  magnitude {magnitude:g}: scale exponents {e.tolist()}")
+    np.testing.assert_array_equal(sexp.cpu().numpy(), e)
+    ref = orc.fp8_quantize(y, e)
     ref_bits = torch.from_numpy(ref.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     np.testing.assert_array_equal(codes.cpu().numpy(), ref_bits)
 

@@ -81,10 +81,7 @@ def _proj_check(inp, Wp, precision, tag):
     gate = inp.gate.numpy().astype(np.float64)
     qs, ks = q, k
     if precision == "bf16_fp8qk":
-        amq = orc.fp8_head_scales(q.astype(np.float32))
-        amk = orc.fp8_head_scales(k.astype(np.float32))
-        qs = orc.fp8_quantize(q.astype(np.float32), amq) * (amq / 448.0)[None, None, :, None]
-        ks = orc.fp8_quantize(k.astype(np.float32), amk) * (amk / 448.0)[None, None, :, None]
+        qs, ks = orc.fp8_qk_operands(q, k, q.shape[-1])
     Os = orc.softmax_branch(qs, ks, v)
     Sf, Sb = orc.vda_states(k, v, beta)
     Ol = orc.linear_branch(q, Sf, Sb)

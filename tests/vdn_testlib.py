@@ -66,8 +66,9 @@ def rel_err(x, ref, head_axis=2):
 
 def oracle_slices(inp: Inputs, frames, heads, tokens=None, fp8=False):
     """Oracle O_soft, O_lin (ungated) and O on the sampled frames / tokens / heads.
-    With fp8=True the softmax uses the E4M3-quantised q and k (per-head scale
-    amax/448), isolating the kernel's error from the quantisation."""
+    With fp8=True the softmax uses the E4M3-quantised q and k (the oracle's fp8
+    operands: per-head power-of-two scales, q carrying the base-2 temperature),
+    isolating the kernel's error from the quantisation."""
     q = inp.host64("q", heads=heads)
     k = inp.host64("k", heads=heads)
     v = inp.host64("v", heads=heads)
@@ -75,12 +76,7 @@ def oracle_slices(inp: Inputs, frames, heads, tokens=None, fp8=False):
     gate = inp.gate.numpy().astype(np.float64)[heads]
     qs, ks = q, k
     if fp8:
-        amq = orc.fp8_head_scales(q.astype(np.float32))
-        amk = orc.fp8_head_scales(k.astype(np.float32))
-        sq = amq.astype(np.float64) / 448.0
-        sk = amk.astype(np.float64) / 448.0
-        qs = orc.fp8_quantize(q.astype(np.float32), amq) * sq[None, None, :, None]
-        ks = orc.fp8_quantize(k.astype(np.float32), amk) * sk[None, None, :, None]
+        qs, ks = orc.fp8_qk_operands(q, k, q.shape[-1])
     O_soft = orc.softmax_branch(qs, ks, v, frames=frames, tokens=tokens)
     Sf, Sb = orc.vda_states(k, v, beta)
     qt = q if tokens is None else q[:, list(tokens)]
