@@ -976,12 +976,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   }
   const uint16_t* Wp = kargs->W;
   const bool lin = it.split < 0 && Wp != nullptr;    // workgroup-uniform
-  // q rows in bf16 as they are stored (the B operand of W q^T): loaded here, beside
-  // the W tile, so the readout sees q rounded once, as the standalone readout does
-  // (the resident Q fragments of the bf16 path carry log2(e)/sqrt(d) and an extra
-  // rounding; the fp8 path's are E4M3 codes)
-  constexpr int QS = D / 16;
-  bf16x8 qr[QS];
   if (lin) {
     const int chunk = it.q_tok0 / N / kChunk;      // chunk of the item's first (and every) row
     const uint16_t* wsrc = Wp + ((size_t)chunk * H + h) * (size_t)(D * D);
@@ -995,10 +989,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (lds_void_ptr)(smem + 1024 * (x * NW + w)), 16,
                                                (uint32_t)(row * 2 * D + 16 * c), 0, 0, 0);
     }
-    const uint16_t* qrow = static_cast<const uint16_t*>(kargs->q) + (size_t)(it.q_tok0 + qi) * rs + (size_t)h * D;
-#pragma unroll
-    for (int s = 0; s < QS; ++s)
-      qr[s] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hf) : bf16x8{};
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -1007,6 +997,20 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   float inv = 1.f / l_tot;
   if constexpr (SPLIT) {
     if (lin) {
+      constexpr int QS = D / 16;
+      bf16x8 qr[QS];
+      float us;
+      if constexpr (FP8) {
+        const uint16_t* q = static_cast<const uint16_t*>(a.q);
+#pragma unroll
+        for (int s = 0; s < QS; ++s)
+          qr[s] = qvalid ? *reinterpret_cast<const bf16x8*>(q + qoff + 16 * s + 8 * hf) : bf16x8{};
+        us = 1.f;
+      } else {
+#pragma unroll
+        for (int s = 0; s < QS; ++s) qr[s] = qb[s];
+        us = 1.f / kargs->scale_log2;
+      }
       // token stride 2 H D: O_soft at h D, g (.) O_lin at H D + h D
       uint16_t* ao = static_cast<uint16_t*>(kargs->O) + (size_t)(it.q_tok0 + qi) * (2 * rs) + (size_t)h * D;
 #pragma unroll
@@ -1024,7 +1028,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
                 make_uint2(pack_bf16x2(c[4 * g + 0] * inv, c[4 * g + 1] * inv),
                            pack_bf16x2(c[4 * g + 2] * inv, c[4 * g + 3] * inv));
             *reinterpret_cast<uint2*>(ao + rs + dd) =
-                make_uint2(pack_bf16x2(acc[4 * g + 0], acc[4 * g + 1]), pack_bf16x2(acc[4 * g + 2], acc[4 * g + 3]));
+                make_uint2(pack_bf16x2(acc[4 * g + 0] * us, acc[4 * g + 1] * us),
+                           pack_bf16x2(acc[4 * g + 2] * us, acc[4 * g + 3] * us));
           }
         }
       }
@@ -1032,6 +1037,26 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
     }
   }
   if (lin) {
+    // Q in bf16 as the B operand: the bf16 path's resident fragments carry the
+    // factor log2(e)/sqrt(d) (rounded to bf16 with it), taken back out of the
+    // product; the fp8 path reads q.  (A version that read q rows in the bf16 path
+    // too, for a single rounding of q, compiled the tile loop differently and ran
+    // 1.9 % slower with twice the L2-miss traffic, same-box A/B; the fragments'
+    // extra rounding is at most 2^-9 relative per q entry.)
+    constexpr int QS = D / 16;
+    bf16x8 qr[QS];
+    float us;
+    if constexpr (FP8) {
+      const uint16_t* q = static_cast<const uint16_t*>(a.q);
+#pragma unroll
+      for (int s = 0; s < QS; ++s)
+        qr[s] = qvalid ? *reinterpret_cast<const bf16x8*>(q + qoff + 16 * s + 8 * hf) : bf16x8{};
+      us = 1.f;
+    } else {
+#pragma unroll
+      for (int s = 0; s < QS; ++s) qr[s] = qb[s];
+      us = 1.f / kargs->scale_log2;
+    }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       floatx16 acc = floatx16{};
@@ -1039,7 +1064,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       for (int s = 0; s < QS; ++s)
         acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(smem + (32 * db + j) * WP + 16 * (2 * s + hf)), qr[s], acc);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] = fmaf(o[db][r], inv, acc[r]);
+      for (int r = 0; r < 16; ++r) o[db][r] = fmaf(acc[r], us, o[db][r] * inv);
     }
     inv = 1.f;
   }

@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256, 1) void attn_w64_kernel(AttnArgs a) {
   const unsigned char* kbase = FP8 ? reinterpret_cast<const unsigned char*>(a.k8)
                                    : static_cast<const unsigned char*>(a.k);
   auto frame_of = [&](int slot) {
-    return it.mode == 0 ? it.k_f0 + slot : chunk_key_frame(slot, it.wf, it.we, F);
+    return it.mode == 0 ? it.k_f0 + slot : chunk_key_frame_sel(slot, it.wf, it.we, F);
   };
   constexpr int KX = (Cfg::K_INSTR + NW - 1) / NW, VX = (Cfg::V_INSTR + NW - 1) / NW;
   constexpr int PAD = NSTG * Cfg::STAGE;             // byte offset of the pad

@@ -72,8 +72,17 @@ constexpr float kLazy = 8.f;   // log2 headroom before the running max is raised
 
 // Frame of slot `s` in the key-frame list of a chunk item: the first frame (if not
 // in the window), the window frames, the last frame (if not in the window).
-// (Written with selects only: the tile loops call it in straight-line code.)
 __device__ inline int chunk_key_frame(int s, int wf, int we, int F) {
+  if (wf > 0) {
+    if (s == 0) return 0;
+    --s;
+  }
+  if (s < we - wf) return wf + s;
+  return F - 1;
+}
+// The same, written with selects only (for tile loops that call it in
+// straight-line code)
+__device__ inline int chunk_key_frame_sel(int s, int wf, int we, int F) {
   const int sw = wf > 0 ? s - 1 : s;                  // slot among the window frames
   const int f = sw < we - wf ? wf + sw : F - 1;
   return (wf > 0 && s == 0) ? 0 : f;
