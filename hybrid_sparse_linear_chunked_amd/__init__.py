@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_PKG, "libvdn_hybrid_attn.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5
 NOALLOC_SCRATCH_BYTES = 64 << 20          # VDN_NOALLOC_SCRATCH_BYTES
-PREC_FP32, PREC_BF16, PREC_BF16_FP8QK = 0, 1, 2
-PRECISIONS = {"fp32": PREC_FP32, "bf16": PREC_BF16, "bf16_fp8qk": PREC_BF16_FP8QK}
+PREC_FP32, PREC_BF16, PREC_BF16_FP8QK, PREC_FP8 = 0, 1, 2, 3
+PRECISIONS = {"fp32": PREC_FP32, "bf16": PREC_BF16, "bf16_fp8qk": PREC_BF16_FP8QK, "fp8": PREC_FP8}
 SCHED_COLS = 13
 STAGES = ("prep", "factor", "scan", "wprep", "attn", "combine", "readout", "quant", "proj")
 

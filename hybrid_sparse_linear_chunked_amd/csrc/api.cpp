@@ -45,9 +45,9 @@ hipError_t mark(int stage, int which, hipStream_t st) {
 
 int check_shape(int F, int N, int H, int d, int prec) {
   if (F < 1 || N < 1 || H < 1) return VDN_ERR_INVALID_ARG;
-  if (prec < VDN_PREC_FP32 || prec > VDN_PREC_BF16_FP8QK) return VDN_ERR_INVALID_ARG;
+  if (prec < VDN_PREC_FP32 || prec > VDN_PREC_FP8) return VDN_ERR_INVALID_ARG;
   if (d != 32 && d != 64 && d != 128) return VDN_ERR_UNSUPPORTED;
-  if (prec == VDN_PREC_BF16_FP8QK && d == 32) return VDN_ERR_UNSUPPORTED;
+  if (prec >= VDN_PREC_BF16_FP8QK && d == 32) return VDN_ERR_UNSUPPORTED;
   // token indices are 32-bit inside the kernels; grid y/z dimensions carry H
   if (static_cast<long long>(F) * N > (1LL << 30) || H > 65535) return VDN_ERR_UNSUPPORTED;
   return VDN_OK;
@@ -60,7 +60,7 @@ size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 // Extra (text / audio) tokens: bf16 / fp8 only; every token index stays 32-bit.
 int check_extra(int F, int N, int T, int prec) {
   if (T < 0) return VDN_ERR_INVALID_ARG;
-  if (T > 0 && prec == VDN_PREC_FP32) return VDN_ERR_UNSUPPORTED;
+  if (T > 0 && (prec == VDN_PREC_FP32 || prec == VDN_PREC_FP8)) return VDN_ERR_UNSUPPORTED;
   if (static_cast<long long>(F) * N + T > (1LL << 30)) return VDN_ERR_UNSUPPORTED;
   return VDN_OK;
 }
@@ -98,11 +98,11 @@ Layout layout(int F, int N, int H, int d, int prec, int T = 0) {
   const size_t rows = na * N + static_cast<size_t>(T);      // split rows per head: anchors, extras
   L.pO = take(static_cast<size_t>(nsplit) * H * rows * d * 4);
   L.pml = take(static_cast<size_t>(nsplit) * H * rows * 2 * 4);
-  if (prec == VDN_PREC_BF16_FP8QK) {
+  if (prec >= VDN_PREC_BF16_FP8QK) {
     const size_t ntok = static_cast<size_t>(F) * N + T;
     L.q8 = take(ntok * H * d);
     L.k8 = take(ntok * H * d);
-    L.fexp = take(2 * static_cast<size_t>(H) * 4);
+    L.fexp = take(3 * static_cast<size_t>(H) * 4);        // q, k, v scale exponents
   }
   L.total = off;
   return L;
@@ -125,6 +125,22 @@ int check_ws(int F, int N, int H, int d, int prec, void* ws, size_t ws_bytes, La
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 // ---- pieces of the launch sequence
+// v laid out for the softmax branch (bf16 vt; with fp8 P.V, E4M3 codes in the vt8
+// layout after v's per-head scale exponents), and with grams the frame Grams
+int launch_vt(const void* k, const void* v, int F, int N, int H, int d, int prec, float* G, float* B, int grams,
+              const Layout& L, WsPtr ws, hipStream_t st) {
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  if (prec == VDN_PREC_FP8) {
+    int* vexp = ws.at<int>(L.fexp) + 2 * H;
+    VDN_TRY(vdn::launch_fp8_scale(v16, F, N, H, d, 1.f, vexp, st));
+    VDN_TRY(vdn::launch_prep(k16, v16, F, N, H, d, nullptr, G, B, grams, st, ws.at<uint8_t>(L.vt), vexp));
+  } else {
+    VDN_TRY(vdn::launch_prep(k16, v16, F, N, H, d, ws.at<uint16_t>(L.vt), G, B, grams, st));
+  }
+  return VDN_OK;
+}
+
 // W: bf16 readout weights to fold into the attention epilogue (O = O_soft + W q on
 // the non-anchor frames), or null for O = O_soft.  T: extra tokens after the video
 // tokens of q, k, v, O (0: none).  split: O is [F*N][2][H][d], O_soft then W q
@@ -135,7 +151,7 @@ int run_softmax(const void* q, const void* k, const void* v, int F, int N, int H
   const uint8_t* q8 = nullptr;
   const uint8_t* k8 = nullptr;
   const int* fexp = nullptr;
-  if (prec == VDN_PREC_BF16_FP8QK) {
+  if (prec >= VDN_PREC_BF16_FP8QK) {
     // per-head power-of-two scales over every token of the layer (the quantiser
     // sees F*N+T tokens as one frame); q is quantised after its multiplication by
     // the base-2 softmax temperature, so the Q.K^T MFMAs deliver log2 units
@@ -150,10 +166,12 @@ int run_softmax(const void* q, const void* k, const void* v, int F, int N, int H
     k8 = ws.at<uint8_t>(L.k8);
     fexp = ws.at<int>(L.fexp);
   }
-  if (prec != VDN_PREC_FP32 && !vt_ready)
-    VDN_STAGE(VDN_STAGE_PREP, st,
-              vdn::launch_prep(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), F, N, H,
-                               d, ws.at<uint16_t>(L.vt), nullptr, nullptr, 0, st));
+  if (prec != VDN_PREC_FP32 && !vt_ready) {
+    VDN_TRY(mark(VDN_STAGE_PREP, 0, st));
+    const int s = launch_vt(k, v, F, N, H, d, prec, nullptr, nullptr, 0, L, ws, st);
+    if (s != VDN_OK) return s;
+    VDN_TRY(mark(VDN_STAGE_PREP, 1, st));
+  }
   if (T > 0) {
     // the extra tokens' V^T blocks, laid out as one more frame of T tokens (no
     // Grams; a few microseconds, outside the stage brackets)
@@ -161,7 +179,7 @@ int run_softmax(const void* q, const void* k, const void* v, int F, int N, int H
     VDN_TRY(vdn::launch_prep(static_cast<const uint16_t*>(k) + voff, static_cast<const uint16_t*>(v) + voff, 1, T,
                              H, d, ws.at<uint16_t>(L.vtx), nullptr, nullptr, 0, st));
   }
-  const int kprec = prec == VDN_PREC_FP32 ? 0 : (prec == VDN_PREC_BF16 ? 1 : 2);
+  const int kprec = prec;      // 0 fp32, 1 bf16, 2 fp8 q.k, 3 fp8 q.k and P.V
   VDN_STAGE(VDN_STAGE_ATTN, st,
             vdn::launch_attn(kprec, q, k, v, ws.at<uint16_t>(L.vt), q8, k8, fexp, F, N, H, d, O,
                              ws.at<float>(L.pO), ws.at<float>(L.pml), W, T, ws.at<uint16_t>(L.vtx), split,
@@ -182,10 +200,12 @@ int run_states(const void* k, const void* v, const float* beta, int F, int N, in
     VDN_STAGE(VDN_STAGE_PREP, st,
               vdn::launch_gram_f32(static_cast<const float*>(k), static_cast<const float*>(v), F, N, H, d,
                                    G, B, st));
-  else
-    VDN_STAGE(VDN_STAGE_PREP, st,
-              vdn::launch_prep(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), F, N, H,
-                               d, ws.at<uint16_t>(L.vt), G, B, 1, st));
+  else {
+    VDN_TRY(mark(VDN_STAGE_PREP, 0, st));
+    const int s = launch_vt(k, v, F, N, H, d, prec, G, B, 1, L, ws, st);
+    if (s != VDN_OK) return s;
+    VDN_TRY(mark(VDN_STAGE_PREP, 1, st));
+  }
   VDN_STAGE(VDN_STAGE_FACTOR, st, vdn::launch_factor(G, B, beta, F, H, d, st));
   VDN_STAGE(VDN_STAGE_SCAN, st, vdn::launch_scan(G, B, F, H, d, Sf, Sb, st));
   return VDN_OK;
@@ -345,7 +365,7 @@ size_t layer_ws_proj(const Layout& L, int F, int N, int H, int d) {
 
 size_t vdn_workspace_bytes_proj(int F, int N, int H, int d, int D, int precision) {
   if (check_shape(F, N, H, d, precision) != VDN_OK) return 0;
-  if (precision == VDN_PREC_FP32 || D < 8 || D % 8 != 0) return 0;
+  if (precision == VDN_PREC_FP32 || precision == VDN_PREC_FP8 || D < 8 || D % 8 != 0) return 0;
   return layer_ws_proj(layout(F, N, H, d, precision), F, N, H, d);
 }
 
@@ -354,7 +374,7 @@ int vdn_hybrid_attn_proj(const void* q, const void* k, const void* v, const floa
                          void* workspace, size_t workspace_bytes, void* stream) {
   int s = check_shape(F, N, H, d, precision);
   if (s != VDN_OK) return s;
-  if (precision == VDN_PREC_FP32) return VDN_ERR_UNSUPPORTED;
+  if (precision == VDN_PREC_FP32 || precision == VDN_PREC_FP8) return VDN_ERR_UNSUPPORTED;
   if (D < 8 || D % 8 != 0) return VDN_ERR_UNSUPPORTED;
   if (static_cast<long long>(256) * 2 * (2LL * H * d) >= (1LL << 32)) return VDN_ERR_UNSUPPORTED;
   if (!q || !k || !v || !beta || !gate || !Wp || !Y) return VDN_ERR_INVALID_ARG;

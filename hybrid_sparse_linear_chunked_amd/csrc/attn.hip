@@ -37,10 +37,38 @@ __device__ inline int vt_pos_of_key(int n) {   // n in [0, 64)
   return 16 * u + 8 * ((r & 7) >> 2) + 4 * (r >> 3) + (r & 3);
 }
 
+// E4M3 ("FN": no infinities, max 448), round to nearest even, saturating.
+__device__ inline uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t code;
+  if (!(a < 448.f)) {
+    code = 0x7Eu;                                   // +-448
+  } else if (a < 0.015625f) {                       // below 2^-6: spacing 2^-9
+    code = static_cast<uint32_t>(__builtin_rintf(a * 512.f));   // 0..8 (8 = 2^-6)
+  } else {
+    const int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xFF) - 127;   // -6..8
+    const float m = __builtin_rintf(a * __builtin_ldexpf(1.f, 3 - e));         // 8..16
+    code = static_cast<uint32_t>((e + 7) * 8 + static_cast<int>(m) - 8);
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return sign | code;
+}
+
+// v transposed as E4M3 codes ("vt8", fp8 P.V): bytes [H][F][nb][D][64], the same
+// blocks and keys as vt, each row regrouped so that a lane half's 32 operand bytes
+// are contiguous:
+//   byte 32 hf + 8 u + e  <->  vt position 16 u + 8 hf + e   (hf = 0, 1; u = 0..3),
+// i.e. lane half hf of a 64-deep P.V MFMA reads bytes 32 hf .. 32 hf + 31, the keys
+// whose probabilities that lane half holds, in the same order.  code =
+// E4M3(fp32(v * 2^-e_v)), e_v the head's power-of-two scale exponent.
+
 // ============================================================ prep (bf16)
 // grid (F, H), 512 threads.  LDS: K^T and V^T of one 64-token tile, keys permuted
 // as in the vt layout (the Gram products only need both operands in the same
-// token order).
+// token order).  With vt8 set, the V^T blocks go out as E4M3 codes in the vt8
+// layout (scale exponents vexp [H]) instead of bf16 vt.
 //
 // The transpose happens in registers: a thread loads four token rows x 8
 // channels (four 16-byte pieces, coalesced across the wave), regroups them into
@@ -54,7 +82,8 @@ __global__ __launch_bounds__(512) void prep_kernel(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ v, int F, int N,
                                                    int H, uint16_t* __restrict__ vt,
                                                    float* __restrict__ G, float* __restrict__ B,
-                                                   int do_grams) {
+                                                   int do_grams, uint8_t* __restrict__ vt8,
+                                                   const int* __restrict__ vexp) {
   constexpr int P = 64 + 8;                      // LDS row pitch (bf16)
   constexpr int NB = D / 32;                     // 32-channel blocks per side
   constexpr int NBLK = 2 * NB * NB;              // G blocks then B blocks
@@ -115,12 +144,28 @@ __global__ __launch_bounds__(512) void prep_kernel(const uint16_t* __restrict__ 
     __syncthreads();
     if (b + 1 < nb) load(b + 1);
     // ---- V^T block out: D rows x 64 keys
-    {
+    if (vt8 == nullptr) {
       uint16_t* dst = vt + (((size_t)h * F + f) * nb + b) * (size_t)(D * 64);
       for (int c = tid; c < D * 8; c += 512) {
         const int row = c >> 3, c8 = c & 7;
         *reinterpret_cast<uint4*>(dst + row * 64 + 8 * c8) =
             *reinterpret_cast<const uint4*>(&VT[row * P + 8 * c8]);
+      }
+    } else {
+      // piece c: row, lane half hf, group u -> 8 codes at byte 32 hf + 8 u
+      uint8_t* dst = vt8 + (((size_t)h * F + f) * nb + b) * (size_t)(D * 64);
+      const int ne = -vexp[h];
+      for (int c = tid; c < D * 8; c += 512) {
+        const int row = c >> 3, hf8 = (c >> 2) & 1, u = c & 3;
+        const uint4 x = *reinterpret_cast<const uint4*>(&VT[row * P + 16 * u + 8 * hf8]);
+        const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+        uint32_t out[2] = {0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t bits = (e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16);
+          out[e >> 2] |= f32_to_e4m3(__builtin_ldexpf(__uint_as_float(bits), ne)) << (8 * (e & 3));
+        }
+        *reinterpret_cast<uint2*>(dst + row * 64 + 32 * hf8 + 8 * u) = make_uint2(out[0], out[1]);
       }
     }
     if (grams) {
@@ -654,10 +699,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   // the factor log2(e)/sqrt(d) (rounded once to bf16).  fp8: the q codes carry it
   // (applied before quantisation), and the power-of-two scales of the q and k
   // codes are the MFMA's E8M0 operand scales (sq for Q, sk for K)
-  int sq = 0, sk = 0;
+  int sq = 0, sk = 0, sv = 0;
   if constexpr (FP8) {
     sq = a.fexp[h] + 127;
     sk = a.fexp[H + h] + 127;
+    if constexpr (Cfg::FP8V) sv = a.fexp[2 * H + h] + 127;
   } else {
     const float scale = a.scale_log2;
 #pragma unroll
@@ -694,8 +740,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
 #pragma unroll
   for (int x = 0; x < VX; ++x) {
     const int q = 64 * (x * NW + w) + lane;
-    const int row = min(q / 9, D - 1), c = min(q % 9, 7);
-    voff[x] = (uint32_t)(row * 128 + 16 * c);
+    const int row = min(q / (Cfg::VCH + 1), D - 1), c = min(q % (Cfg::VCH + 1), Cfg::VCH - 1);
+    voff[x] = (uint32_t)(row * (16 * Cfg::VCH) + 16 * c);
   }
   // loads [x0, x1) of this wave's share of a tile: K loads first, then V^T loads
   constexpr int LPT = KX + VX;
@@ -714,10 +760,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       if (x * NW + w >= Cfg::K_INSTR) break;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_ptr)(sbase + 1024 * (x * NW + w)), 16, koff[x], 0, 0, 0);
     }
-    const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(
-        XT && f == F ? a.vtx + ((size_t)h * a.nbx + b) * (size_t)(D * BK)
-                     : a.vt + (((size_t)h * F + f) * nb + b) * (size_t)(D * BK));
-    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vsrc, (uint32_t)(D * BK * 2));
+    // (fp8 P.V: vt holds the E4M3 codes of v, one byte per element)
+    constexpr int VEB = Cfg::FP8V ? 1 : 2;
+    const unsigned char* vsrc =
+        XT && f == F ? reinterpret_cast<const unsigned char*>(a.vtx + ((size_t)h * a.nbx + b) * (size_t)(D * BK))
+                     : reinterpret_cast<const unsigned char*>(a.vt) + (((size_t)h * F + f) * nb + b) * (size_t)(D * BK * VEB);
+    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vsrc, (uint32_t)(D * BK * VEB));
 #pragma unroll
     for (int x = 0; x < VX; ++x) {
       if (KX + x < x0 || KX + x >= x1) continue;
@@ -829,7 +877,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       if (bt + 1 < NQB) {
 #pragma unroll
         for (int x = 0; x < QB; ++x) kf[(bt + 1) & 1][x] = Cfg::kfrag(sbase, (bt + 1) * QB + x, j, hf);
-      } else {
+      } else if constexpr (!Cfg::FP8V) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) va[0][db] = Cfg::vfrag(vbase, 0, db, j, hf);
       }
@@ -889,6 +937,33 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
     // exponent of a score: the scores are already s - m in log2 units
     auto expo = [&](float x) { return __builtin_amdgcn_exp2f(x); };
 
+    if constexpr (Cfg::FP8V) {
+      // ---- O^T += V^T P^T on E4M3 codes: one 64-deep MFMA per 32-channel block
+      // covers the tile's 64 keys.  Lane (j, hf) holds the probabilities of query j
+      // for keys 32 kb + 8 (r / 4) + 4 hf + r % 4 (kb = 0, 1; r = 0..15), packed as
+      // bytes 16 kb + r of its B operand; the vt8 layout puts the same keys at the
+      // same bytes of the lane's V^T operand.  P is in (0, 2^kLazy], inside E4M3's
+      // range; the row sum takes the unrounded fp32 probabilities.
+      intx8 vf8[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vf8[db] = Cfg::vfrag8(vbase, db, j, hf);
+      float psum = 0.f;
+      intx8 pf;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int kb = t >> 2, r0 = 4 * (t & 3);
+        const float p0 = expo(s[kb][r0]), p1 = expo(s[kb][r0 + 1]);
+        const float p2 = expo(s[kb][r0 + 2]), p3 = expo(s[kb][r0 + 3]);
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
+        pf[t] = wd;
+        psum += (p0 + p1) + (p2 + p3);
+      }
+      lds_wait_all();
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] = mfma_fp8_scaled(vf8[db], pf, o[db], sv, 127);
+      l_run += psum;
+    } else {
     // ---- O^T += V^T P^T, one group of 16 keys per batch; the probabilities of
     // the next group are formed on the VALU while this group's MFMAs run, and
     // the row sum l takes the same bf16 values, two per v_dot2_f32_bf16
@@ -928,6 +1003,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run += psum;
+    }
 
     if ((t & (AHEAD - 1)) == AHEAD - 1 || t + 1 == ntiles) {
       __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next tiles landed
@@ -1155,24 +1231,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // ============================================================ fp8 quantiser
-// E4M3 ("FN": no infinities, max 448), round to nearest even, saturating.
-__device__ inline uint32_t f32_to_e4m3(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = fabsf(x);
-  uint32_t code;
-  if (!(a < 448.f)) {
-    code = 0x7Eu;                                   // +-448
-  } else if (a < 0.015625f) {                       // below 2^-6: spacing 2^-9
-    code = static_cast<uint32_t>(__builtin_rintf(a * 512.f));   // 0..8 (8 = 2^-6)
-  } else {
-    const int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xFF) - 127;   // -6..8
-    const float m = __builtin_rintf(a * __builtin_ldexpf(1.f, 3 - e));         // 8..16
-    code = static_cast<uint32_t>((e + 7) * 8 + static_cast<int>(m) - 8);
-    if (code > 0x7Eu) code = 0x7Eu;
-  }
-  return sign | code;
-}
 
 __global__ void fill_u32_kernel(uint32_t* p, int n, uint32_t value) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -1255,17 +1313,18 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
 // ============================================================ launchers
 template <int D>
 static hipError_t prep_d(const uint16_t* k, const uint16_t* v, int F, int N, int H, uint16_t* vt,
-                         float* G, float* B, int grams, hipStream_t st) {
-  hipLaunchKernelGGL(prep_kernel<D>, dim3(F, H), dim3(512), 0, st, k, v, F, N, H, vt, G, B, grams);
+                         float* G, float* B, int grams, uint8_t* vt8, const int* vexp, hipStream_t st) {
+  hipLaunchKernelGGL(prep_kernel<D>, dim3(F, H), dim3(512), 0, st, k, v, F, N, H, vt, G, B, grams, vt8, vexp);
   return hipGetLastError();
 }
 
 hipError_t launch_prep(const uint16_t* k, const uint16_t* v, int F, int N, int H, int D,
-                       uint16_t* vt, float* G, float* B, int grams, hipStream_t st) {
+                       uint16_t* vt, float* G, float* B, int grams, hipStream_t st, uint8_t* vt8,
+                       const int* vexp) {
   switch (D) {
-    case 32: return prep_d<32>(k, v, F, N, H, vt, G, B, grams, st);
-    case 64: return prep_d<64>(k, v, F, N, H, vt, G, B, grams, st);
-    case 128: return prep_d<128>(k, v, F, N, H, vt, G, B, grams, st);
+    case 32: return prep_d<32>(k, v, F, N, H, vt, G, B, grams, vt8, vexp, st);
+    case 64: return prep_d<64>(k, v, F, N, H, vt, G, B, grams, vt8, vexp, st);
+    case 128: return prep_d<128>(k, v, F, N, H, vt, G, B, grams, vt8, vexp, st);
   }
   return hipErrorInvalidValue;
 }
@@ -1296,6 +1355,12 @@ static hipError_t attn_f32(const AttnArgs& a, hipStream_t st) {
 template <int D, int PREC>
 static hipError_t attn_lds(const AttnArgs& a, hipStream_t st, bool split) {
   constexpr int lds = kLdsStages * LdsCfg<D, PREC>::STAGE;
+  if constexpr (PREC == 3) {
+    // fp8 P.V: the plain layer only (no extra tokens, no split output)
+    if (split || a.T > 0) return hipErrorInvalidValue;
+    static std::atomic<unsigned long long> done8{0};
+    return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, false>, lds, &done8, a, st, 64 * kLdsWaves);
+  } else {
   if constexpr (D == 128) {
     // opt-in: the 64-queries-per-wave kernel (half the LDS reads per MFMA, one
     // wave per SIMD); slower than this one on the measured workloads
@@ -1321,6 +1386,7 @@ static hipError_t attn_lds(const AttnArgs& a, hipStream_t st, bool split) {
   }
   static std::atomic<unsigned long long> done{0};
   return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, false>, lds, &done, a, st, 64 * kLdsWaves);
+  }
 }
 
 hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, const uint16_t* vt,
@@ -1355,6 +1421,9 @@ hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, co
   } else if (prec == 2) {
     if (D == 64) return attn_lds<64, 2>(a, st, split != 0);
     if (D == 128) return attn_lds<128, 2>(a, st, split != 0);
+  } else if (prec == 3) {
+    if (D == 64) return attn_lds<64, 3>(a, st, split != 0);
+    if (D == 128) return attn_lds<128, 3>(a, st, split != 0);
   }
   return hipErrorInvalidValue;
 }
@@ -1383,28 +1452,29 @@ hipError_t launch_combine(int prec, const float* part_O, const float* part_ml, i
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fp8_quant(const uint16_t* x, int F, int N, int H, int D, float prescale, uint8_t* codes,
-                            int* fexp, hipStream_t st) {
+hipError_t launch_fp8_scale(const uint16_t* x, int F, int N, int H, int D, float prescale, int* fexp,
+                            hipStream_t st) {
   const size_t ntok = (size_t)F * N;
   uint32_t* bits = reinterpret_cast<uint32_t*>(fexp);
   hipLaunchKernelGGL(fill_u32_kernel, dim3((H + 255) / 256), dim3(256), 0, st, bits, H, 0u);
   const dim3 g1((unsigned)((ntok + 1023) / 1024), H);
-  const size_t n8 = ntok * H * D / 8;
-  const dim3 g2((unsigned)((n8 + 255) / 256));
   switch (D) {
-    case 64:
-      hipLaunchKernelGGL(amax_kernel<64>, g1, dim3(256), 0, st, x, ntok, H, bits);
-      hipLaunchKernelGGL(fp8_exp_kernel, dim3((H + 63) / 64), dim3(64), 0, st, bits, H, prescale);
-      hipLaunchKernelGGL(quant_kernel<64>, g2, dim3(256), 0, st, x, n8, H, fexp, prescale, codes);
-      break;
-    case 128:
-      hipLaunchKernelGGL(amax_kernel<128>, g1, dim3(256), 0, st, x, ntok, H, bits);
-      hipLaunchKernelGGL(fp8_exp_kernel, dim3((H + 63) / 64), dim3(64), 0, st, bits, H, prescale);
-      hipLaunchKernelGGL(quant_kernel<128>, g2, dim3(256), 0, st, x, n8, H, fexp, prescale, codes);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 64: hipLaunchKernelGGL(amax_kernel<64>, g1, dim3(256), 0, st, x, ntok, H, bits); break;
+    case 128: hipLaunchKernelGGL(amax_kernel<128>, g1, dim3(256), 0, st, x, ntok, H, bits); break;
+    default: return hipErrorInvalidValue;
   }
+  hipLaunchKernelGGL(fp8_exp_kernel, dim3((H + 63) / 64), dim3(64), 0, st, bits, H, prescale);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_quant(const uint16_t* x, int F, int N, int H, int D, float prescale, uint8_t* codes,
+                            int* fexp, hipStream_t st) {
+  hipError_t e = launch_fp8_scale(x, F, N, H, D, prescale, fexp, st);
+  if (e != hipSuccess) return e;
+  const size_t n8 = (size_t)F * N * H * D / 8;
+  const dim3 g2((unsigned)((n8 + 255) / 256));
+  if (D == 64) hipLaunchKernelGGL(quant_kernel<64>, g2, dim3(256), 0, st, x, n8, H, fexp, prescale, codes);
+  else hipLaunchKernelGGL(quant_kernel<128>, g2, dim3(256), 0, st, x, n8, H, fexp, prescale, codes);
   return hipGetLastError();
 }
 

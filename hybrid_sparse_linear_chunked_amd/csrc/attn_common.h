@@ -26,7 +26,7 @@ struct AttnArgs {
   const uint16_t* vt;     // bf16 / fp8 paths: transposed v
   const uint8_t* q8;      // fp8 path: E4M3 codes
   const uint8_t* k8;
-  const int* fexp;        // fp8 path: [2][H] power-of-two scale exponents (q then k)
+  const int* fexp;        // fp8 paths: [3][H] power-of-two scale exponents (q, k, v)
   void* O;
   float* part_O;          // [nsplit][H][na][N][D]
   float* part_ml;         // [nsplit][H][na][N][2]
@@ -99,13 +99,15 @@ __device__ inline int chunk_key_frame_sel(int s, int wf, int we, int F) {
 // plus an immediate offset.
 template <int D, int PREC>
 struct LdsCfg {
-  static constexpr bool FP8 = PREC == 2;
+  static constexpr bool FP8 = PREC >= 2;           // q.k on E4M3 codes
+  static constexpr bool FP8V = PREC == 3;          // P.V on E4M3 codes too
   static constexpr int KROW = FP8 ? D : 2 * D;     // bytes per K row in global memory
   static constexpr int KCH = KROW / 16;            // 16-byte chunks per K row
   static constexpr int KP = 16 * (KCH + 1);        // LDS pitch of a K row
-  static constexpr int VP = 16 * 9;                // LDS pitch of a V^T row (64 keys bf16 + pad)
+  static constexpr int VCH = FP8V ? 4 : 8;         // 16-byte chunks of a V^T row (64 keys)
+  static constexpr int VP = 16 * (VCH + 1);        // LDS pitch of a V^T row (+ pad)
   static constexpr int K_INSTR = KCH + 1;          // wave-wide direct loads per K tile (64 rows)
-  static constexpr int V_INSTR = (9 * D + 63) / 64;
+  static constexpr int V_INSTR = ((VCH + 1) * D + 63) / 64;
   static constexpr int K_BYTES = 1024 * K_INSTR;
   static constexpr int V_BYTES = 1024 * V_INSTR;
   static constexpr int STAGE = K_BYTES + V_BYTES;
@@ -129,6 +131,14 @@ struct LdsCfg {
   // LDS operand of one P.V MFMA: V^T rows 32*db + (lane & 31), keys 16u..16u+15
   __device__ static bf16x8 vfrag(const unsigned char* vbase, int u, int db, int j, int hf) {
     return *reinterpret_cast<const bf16x8*>(vbase + (32 * db + j) * VP + 16 * (2 * u + hf));
+  }
+  // fp8 P.V: V^T rows 32*db + (lane & 31), the 32 codes of lane half hf (all 64 keys
+  // of the tile in one 64-deep MFMA; see the vt8 layout)
+  __device__ static intx8 vfrag8(const unsigned char* vbase, int db, int j, int hf) {
+    const unsigned char* row = vbase + (32 * db + j) * VP + 32 * hf;
+    const uint4 x0 = *reinterpret_cast<const uint4*>(row);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(row + 16);
+    return intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
   }
 };
 

@@ -30,8 +30,11 @@ inline hipError_t set_max_lds_once(const void* fn, int lds, std::atomic<unsigned
 hipError_t launch_proj(const uint16_t* A, const uint16_t* B, int M, int N, int K, uint16_t* Y, hipStream_t st);
 
 // attn.hip
+// vt8 (optional): V^T as E4M3 codes in the vt8 layout, with scale exponents vexp [H],
+// instead of bf16 vt
 hipError_t launch_prep(const uint16_t* k, const uint16_t* v, int F, int N, int H, int D,
-                       uint16_t* vt, float* G, float* B, int grams, hipStream_t st);
+                       uint16_t* vt, float* G, float* B, int grams, hipStream_t st, uint8_t* vt8 = nullptr,
+                       const int* vexp = nullptr);
 hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, const uint16_t* vt,
                        const uint8_t* q8, const uint8_t* k8, const int* fexp, int F, int N, int H,
                        int D, void* O, float* part_O, float* part_ml, const uint16_t* W,
@@ -41,6 +44,9 @@ hipError_t launch_combine(int prec, const float* part_O, const float* part_ml, i
 // The softmax temperature in base-2 units, log2(e) / sqrt(d), in fp32 (the bf16
 // Q operand and the fp8 q codes carry it)
 inline float softmax_temperature_log2(int d) { return 1.4426950408889634f / sqrtf(static_cast<float>(d)); }
+// per-head power-of-two scale exponents of fp32(x * prescale) into fexp [H]
+hipError_t launch_fp8_scale(const uint16_t* x, int F, int N, int H, int D, float prescale, int* fexp,
+                            hipStream_t st);
 hipError_t launch_fp8_quant(const uint16_t* x, int F, int N, int H, int D, float prescale, uint8_t* codes,
                             int* fexp, hipStream_t st);
 void attn_split_plan(int F, int* nsplit, int* fs);

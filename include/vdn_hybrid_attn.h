@@ -69,6 +69,16 @@ extern "C" {
                                       E4M3 codes with per-head power-of-two scales computed
                                       internally (q first multiplied by log2(e)/sqrt(d));
                                       P.V, the VDA branch and the merge as bf16 */
+#define VDN_PREC_FP8         3     /* bf16 I/O; the softmax branch runs on E4M3 codes: q.k as
+                                      in VDN_PREC_BF16_FP8QK, and P.V with v coded per head
+                                      the same way (power-of-two scale, prescale 1) and the
+                                      probabilities rounded to E4M3 after the running-max
+                                      shift (row sums from the unrounded values); the VDA
+                                      branch and the merge as bf16.  d = 64 or 128;
+                                      vdn_hybrid_attn, vdn_hybrid_attn_noalloc,
+                                      vdn_softmax_branch, vdn_vda_states and vdn_vda_linear
+                                      only (the extra-token and projection entry points
+                                      return VDN_ERR_UNSUPPORTED) */
 
 /* Bytes of workspace the calls below need for this shape; 0 if the shape or
  * precision is invalid or unsupported. */

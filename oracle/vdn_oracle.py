@@ -491,3 +491,19 @@ def fp8_qk_operands(q, k, d: int):
     q_eff = fp8_quantize(qp, eq) * sq.reshape((-1, 1))
     k_eff = fp8_quantize(kf, ek) * sk.reshape((-1, 1))
     return q_eff, k_eff
+
+
+def fp8_v_operand(v) -> np.ndarray:
+    """v as the full-fp8 variant's P.V sees it, float64: per head, E4M3 codes of v
+    with the power-of-two scale of fp8_scale_exponent over all tokens (no
+    prescale), times that scale.  v: [..., H, d] (head axis -2).
+
+    Reading (as for fp8_qk_operands, the pages name FP8 inference without its
+    format): v is coded like k; the probabilities are also rounded to E4M3 in that
+    variant, after the shift by the kernel's running maximum, which this oracle
+    does not model (the rounding depends on the running maximum's history), so the
+    variant is compared within the probabilities' rounding bound."""
+    vf = np.asarray(v, dtype=np.float32)
+    ev = fp8_scale_exponent(fp8_head_scales(vf))
+    return fp8_quantize(vf, ev) * np.exp2(ev.astype(np.float64)).reshape((-1, 1))
+

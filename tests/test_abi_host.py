@@ -96,6 +96,10 @@ def test_argument_errors_return_before_launch(lib):
     assert call(A, A, A, None, A, F, N, H, d, 1, A, A, need, None) == vdn.ERR_INVALID_ARG
     assert call(A, A, A, A, A, F, N, H, 48, 1, A, A, need, None) == vdn.ERR_UNSUPPORTED
     assert call(A, A, A, A, A, F, N, H, 32, 2, A, A, need, None) == vdn.ERR_UNSUPPORTED
+    assert call(A, A, A, A, A, F, N, H, 32, 3, A, A, need, None) == vdn.ERR_UNSUPPORTED
+    assert call(A, A, A, A, A, F, N, H, d, 4, A, A, need, None) == vdn.ERR_INVALID_ARG
+    # the full-fp8 workspace holds the fp8-q.k one plus v's scale exponents
+    assert lib.vdn_workspace_bytes(F, N, H, 64, 3) >= lib.vdn_workspace_bytes(F, N, H, 64, 2) > 0
     assert call(A, A, A, A, A, 0, N, H, d, 1, A, A, need, None) == vdn.ERR_INVALID_ARG
     assert call(A, A, A, A, A, F, N, H, d, 7, A, A, need, None) == vdn.ERR_INVALID_ARG
     assert call(A + 2, A, A, A, A, F, N, H, d, 1, A, A, need, None) == vdn.ERR_INVALID_ARG
@@ -127,6 +131,9 @@ def test_mixed_and_projection_argument_errors(lib):
     assert call(A, None, A, A, A, F, N, T, H, d, 1, A, A, need_x, None) == vdn.ERR_INVALID_ARG
     assert call(A, A, A, A, A, F, N, T, H, d, 1, A, A, need_x - 1, None) == vdn.ERR_WORKSPACE
     assert call(A, A, A, A, A, F, N, 1 << 30, H, d, 1, A, A, need_x, None) == vdn.ERR_UNSUPPORTED
+    # the full-fp8 precision covers the plain layer only
+    assert lib.vdn_workspace_bytes_mixed(F, N, T, H, d, vdn.PREC_FP8) == 0
+    assert call(A, A, A, A, A, F, N, T, H, d, vdn.PREC_FP8, A, A, need_x, None) == vdn.ERR_UNSUPPORTED
 
     need_p = lib.vdn_workspace_bytes_proj(F, N, H, d, D, 1)
     assert need_p >= need + F * N * 2 * H * d * 2
@@ -134,6 +141,8 @@ def test_mixed_and_projection_argument_errors(lib):
     assert lib.vdn_workspace_bytes_proj(F, N, H, d, 12, 1) == 0           # D a multiple of 8
     call = lib.vdn_hybrid_attn_proj
     assert call(A, A, A, A, A, A, F, N, H, d, D, 0, A, A, need_p, None) == vdn.ERR_UNSUPPORTED
+    assert call(A, A, A, A, A, A, F, N, H, d, D, vdn.PREC_FP8, A, A, need_p, None) == vdn.ERR_UNSUPPORTED
+    assert lib.vdn_workspace_bytes_proj(F, N, H, d, D, vdn.PREC_FP8) == 0
     assert call(A, A, A, A, A, A, F, N, H, d, 12, 1, A, A, need_p, None) == vdn.ERR_UNSUPPORTED
     assert call(A, A, A, A, A, None, F, N, H, d, D, 1, A, A, need_p, None) == vdn.ERR_INVALID_ARG
     assert call(A, A, A, A, A, A + 8, F, N, H, d, D, 1, A, A, need_p, None) == vdn.ERR_INVALID_ARG

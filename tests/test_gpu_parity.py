@@ -27,7 +27,14 @@ from vdn_testlib import TOL, Inputs, oracle_slices, rel_err
 
 pytestmark = pytest.mark.gpu
 
-PREC = {"fp32": vdn.PREC_FP32, "bf16": vdn.PREC_BF16, "bf16_fp8qk": vdn.PREC_BF16_FP8QK}
+PREC = {"fp32": vdn.PREC_FP32, "bf16": vdn.PREC_BF16, "bf16_fp8qk": vdn.PREC_BF16_FP8QK, "fp8": vdn.PREC_FP8}
+
+# The full-fp8 layer (VDN_PREC_FP8) also rounds the probabilities to E4M3 after the
+# running-max shift, which the oracle does not model: each weight moves by at most
+# half a step of a 3-bit mantissa (2^-4 relative), so O_soft is held to 5e-2 of the
+# oracle fed the same E4M3 q, k, v (measured 2.2-2.3 % on these inputs) and 8e-2 of
+# the unquantised one.
+FP8PV_SOFT_TOL, FP8PV_SOFT_TOL_UNQ = 5e-2, 8e-2
 
 
 def say(*a):
@@ -189,10 +196,12 @@ def test_mid_config_full(mid_layer, heads):
 
 def _fused_softmax_half(inp, precision, frames, heads, tokens, gate_scale=3e-3):
     """(i) g = 0: the layer equals the softmax branch bit for bit; (ii) a small gate,
-    so that O_soft carries most of |O|: the layer matches the oracle (fp8: within
-    1e-2 of the oracle fed the same E4M3 codes and 5e-2 of the unquantised one)."""
+    so that O_soft carries most of |O|: the layer matches the oracle (fp8 q.k: within
+    1e-2 of the oracle fed the same E4M3 codes and 5e-2 of the unquantised one; full
+    fp8: the O_soft tolerances above)."""
     p = PREC[precision]
-    fp8 = precision == "bf16_fp8qk"
+    fp8 = precision in ("bf16_fp8qk", "fp8")
+    fp8v = precision == "fp8"
     O0 = vdn.hybrid_attn(inp.dq, inp.dk, inp.dv, inp.dbeta, torch.zeros_like(inp.dgate), precision=p)
     Os = vdn.softmax_branch(inp.dq, inp.dk, inp.dv, precision=p)
     torch.cuda.synchronize()
@@ -206,17 +215,20 @@ def _fused_softmax_half(inp, precision, frames, heads, tokens, gate_scale=3e-3):
     del O
     g = inp.gate.numpy().astype(np.float64)[heads] * np.float64(np.float32(gate_scale))
     for quant in ((True, False) if fp8 else (False,)):
-        rOs, rOl, _, _, _ = oracle_slices(inp, frames, heads, tokens, fp8=quant)
+        rOs, rOl, _, _, _ = oracle_slices(inp, frames, heads, tokens, fp8=quant, fp8v=quant and fp8v)
         rO = orc.merge(rOs, rOl, g)
         soft_share = np.linalg.norm(rOs) / np.linalg.norm(rO)
         lin_share = np.linalg.norm(g[None, None] * rOl) / np.linalg.norm(rO)
         say(f"  small gate: |O_soft| / |O| = {soft_share:.3f}, |g O_lin| / |O| = {lin_share:.3f}")
         assert soft_share >= 0.3 and lin_share >= 0.1
-        check("O (small gate)" + (" vs E4M3 oracle" if quant else ""), got, rO,
-              1e-2 if (quant or not fp8) else 5e-2)
+        if fp8v:
+            tol = FP8PV_SOFT_TOL if quant else FP8PV_SOFT_TOL_UNQ
+        else:
+            tol = 1e-2 if (quant or not fp8) else 5e-2
+        check("O (small gate)" + (" vs E4M3 oracle" if quant else ""), got, rO, tol)
 
 
-@pytest.mark.parametrize("precision", ["bf16", "bf16_fp8qk"])
+@pytest.mark.parametrize("precision", ["bf16", "bf16_fp8qk", "fp8"])
 def test_fused_softmax_half_mid(precision):
     F, N, H, d = 25, 1024, 3, 128
     say(f"case fused epilogue F={F} N={N} H={H} d={d} {precision}")
@@ -240,6 +252,29 @@ def test_w64_kernel_opt_in(precision, monkeypatch):
     say(f"case w64 fused epilogue F={F} N={N} H={H} d={d} {precision}")
     inp = Inputs(F, N, H, d, precision, seed=11)
     _fused_softmax_half(inp, precision, list(range(F)), list(range(H)), None)
+
+
+@pytest.mark.parametrize("cfg", [
+    (24, 50, 2, 128),     # ragged 64-key tiles and query tile
+    (31, 48, 2, 64),      # d = 64, partial last chunk
+    (7, 40, 2, 128),      # every chunk sees every frame: no linear states
+])
+def test_full_fp8_layer(cfg):
+    F, N, H, d = cfg
+    say(f"case full fp8 F={F} N={N} H={H} d={d}")
+    inp = Inputs(F, N, H, d, "fp8", seed=1)
+    O, Os, Ol, Sf, Sb = run_all(inp, "fp8")
+    fr, hs = list(range(F)), list(range(H))
+    rOs, rOl, rO, rSf, rSb = oracle_slices(inp, fr, hs, fp8=True, fp8v=True)
+    es, eb = _states_err(Sf, rSf), _states_err(Sb, rSb)
+    say(f"  S_fwd {es:.3e}  S_bwd {eb:.3e}")
+    assert es <= STATE_TOL and eb <= STATE_TOL
+    check("O_lin", host(Ol), rOl, 1e-2)
+    check("O_soft vs E4M3 q, k, v oracle", host(Os), rOs, FP8PV_SOFT_TOL)
+    # (with no linear states, as at F = 7, O is O_soft: its tolerance)
+    check("O vs E4M3 q, k, v oracle", host(O), rO, FP8PV_SOFT_TOL)
+    uOs = oracle_slices(inp, fr, hs)[0]
+    check("O_soft vs unquantised oracle", host(Os), uOs, FP8PV_SOFT_TOL_UNQ)
 
 
 def test_determinism():
@@ -295,19 +330,20 @@ def sampled_full_size(F, N, H, d, precision):
     C = (F + 4) // 5
     frames = [0, 1, 7, 12, F // 2, F - 9, F - 2, F - 1]       # anchor, edge, next-to-edge, interior
     tokens = list(range(0, N, 97)) + [N - 1]
-    fp8 = precision == "bf16_fp8qk"
-    rOs, rOl, rO, rSf, rSb = oracle_slices(inp, frames, heads, tokens, fp8=fp8)
+    fp8 = precision in ("bf16_fp8qk", "fp8")
+    fp8v = precision == "fp8"
+    rOs, rOl, rO, rSf, rSb = oracle_slices(inp, frames, heads, tokens, fp8=fp8, fp8v=fp8v)
     say("  oracle done")
     es = _states_err(Sf[:, heads], rSf)
     eb = _states_err(Sb[:, heads], rSb)
     say(f"  S_fwd {es:.3e}  S_bwd {eb:.3e}")
     assert es <= STATE_TOL and eb <= STATE_TOL
-    check("O_soft", host(Os, frames, tokens, heads), rOs, 1e-2)
+    check("O_soft", host(Os, frames, tokens, heads), rOs, FP8PV_SOFT_TOL if fp8v else 1e-2)
     check("O", host(O, frames, tokens, heads), rO, 1e-2)
     if fp8:
-        # against the unquantised oracle: the pages' tolerance for the fp8 variant
+        # against the unquantised oracle
         uOs, _, uO, _, _ = oracle_slices(inp, frames, heads, tokens, fp8=False)
-        check("O_soft vs unquantised", host(Os, frames, tokens, heads), uOs, 5e-2)
+        check("O_soft vs unquantised", host(Os, frames, tokens, heads), uOs, FP8PV_SOFT_TOL_UNQ if fp8v else 5e-2)
         check("O vs unquantised", host(O, frames, tokens, heads), uO, 5e-2)
     del O, Os, Sf, Sb
     # the softmax half of the fused output, at this shape and launch configuration
@@ -320,6 +356,10 @@ def test_headline_config_sampled():
 
 def test_long_stream_fp8_sampled():
     sampled_full_size(180, 4032, 24, 128, "bf16_fp8qk")
+
+
+def test_long_stream_full_fp8_sampled():
+    sampled_full_size(180, 4032, 24, 128, "fp8")
 
 
 def test_binding_rejects_aliasing():

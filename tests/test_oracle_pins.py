@@ -437,7 +437,7 @@ def test_fp8_scale_exponent_is_the_smallest_power_of_two():
 
 
 def test_fp8_quantize_power_of_two_codes():
-    # codes of x / 2^e: every head reaches (224, 448], and code * 2^e is within half
+    # codes of x / 2^e: every head reaches [224, 448], and code * 2^e is within half
     # an E4M3 step of x (relative 2^-4 in the normal range, 2^-10 * 2^e below it)
     F, N, H, d = 10, 8, 3, 16
     q, _, _ = small_inputs(F, N, H, d)
@@ -447,7 +447,7 @@ def test_fp8_quantize_power_of_two_codes():
     back = codes * np.exp2(e.astype(np.float64))[:, None]
     for h in range(H):
         m = np.abs(codes[:, :, h]).max()
-        assert 224.0 < m <= 448.0
+        assert 224.0 <= m <= 448.0     # (the top may round down to 224)
     xs = x.astype(np.float64)
     step = np.maximum(2.0 ** -4 * np.abs(xs), 2.0 ** -10 * np.exp2(e.astype(np.float64))[:, None])
     assert np.all(np.abs(back - xs) <= step * (1 + 1e-12))
@@ -479,3 +479,24 @@ def test_fp8_temperature_and_operands():
     s_ref = np.einsum("fnhd,gmhd->hfngm", q, k)
     bound = np.einsum("fnhd,gmhd->hfngm", np.abs(q) * 2.0 ** -4 + 2.0 ** -10 * unit[None, None, :, None], np.abs(k))
     assert np.all(np.abs(s_eff - s_ref) <= bound * (1 + 1e-5) + 1e-9)
+
+
+def test_fp8_v_operand():
+    # v on the E4M3 grid times 2^-3 with a head maximum of 448 * 2^-3: exact; any v:
+    # within half an E4M3 step, every head reaching [224, 448] code units
+    rng = np.random.default_rng(8)
+    F, N, H, d = 5, 12, 3, 32
+    grid = orc.e4m3_round(rng.uniform(-448, 448, (F, N, H, d)))
+    grid[1, 2, :, 3] = -448.0
+    v = grid / 8.0
+    np.testing.assert_array_equal(orc.fp8_v_operand(v), v)
+    v = (rng.standard_normal((F, N, H, d)) * np.array([1e-4, 1.0, 300.0])[None, None, :, None]).astype(np.float32)
+    ve = orc.fp8_v_operand(v)
+    e = orc.fp8_scale_exponent(orc.fp8_head_scales(v)).astype(np.float64)
+    unit = np.exp2(e)[:, None]
+    vs = v.astype(np.float64)
+    step = np.maximum(2.0 ** -4 * np.abs(vs), 2.0 ** -10 * unit)
+    assert np.all(np.abs(ve - vs) <= step * (1 + 1e-12))
+    for h in range(H):
+        assert 224.0 <= np.abs(ve[:, :, h]).max() / unit[h, 0] <= 448.0   # (the top may round down to 224)
+

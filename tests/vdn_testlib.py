@@ -9,7 +9,7 @@ import torch
 import vdn_synth
 from oracle import vdn_oracle as orc
 
-PREC_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16, "bf16_fp8qk": torch.bfloat16}
+PREC_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16, "bf16_fp8qk": torch.bfloat16, "fp8": torch.bfloat16}
 TOL = {"fp32": 1e-4, "bf16": 1e-2, "bf16_fp8qk": 5e-2}
 
 
@@ -64,7 +64,7 @@ def rel_err(x, ref, head_axis=2):
     return worst
 
 
-def oracle_slices(inp: Inputs, frames, heads, tokens=None, fp8=False):
+def oracle_slices(inp: Inputs, frames, heads, tokens=None, fp8=False, fp8v=False):
     """Oracle O_soft, O_lin (ungated) and O on the sampled frames / tokens / heads.
     With fp8=True the softmax uses the E4M3-quantised q and k (the oracle's fp8
     operands: per-head power-of-two scales, q carrying the base-2 temperature),
@@ -75,9 +75,12 @@ def oracle_slices(inp: Inputs, frames, heads, tokens=None, fp8=False):
     beta = inp.beta.numpy().astype(np.float64)[:, heads]
     gate = inp.gate.numpy().astype(np.float64)[heads]
     qs, ks = q, k
+    vs = v
     if fp8:
         qs, ks = orc.fp8_qk_operands(q, k, q.shape[-1])
-    O_soft = orc.softmax_branch(qs, ks, v, frames=frames, tokens=tokens)
+    if fp8v:
+        vs = orc.fp8_v_operand(v)
+    O_soft = orc.softmax_branch(qs, ks, vs, frames=frames, tokens=tokens)
     Sf, Sb = orc.vda_states(k, v, beta)
     qt = q if tokens is None else q[:, list(tokens)]
     O_lin = orc.linear_branch(qt, Sf, Sb, frames=frames)
