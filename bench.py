@@ -221,6 +221,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default 3; 2 for the two largest)")
     ap.add_argument("--config", type=int, default=3, choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--precision", default=None, choices=["fp32", "bf16", "bf16_fp8qk", "fp8"],
+                    help="run the workload's shape in another precision (fp8: the full-fp8 softmax branch, "
+                         "P.V on E4M3 codes too); the line names the precision in its workload")
     ap.add_argument("--extra-tokens", type=int, default=0, metavar="T",
                     help="append T text / audio tokens to the layer's sequence (no CPU baseline)")
     ap.add_argument("--out-proj", type=int, default=0, metavar="D",
@@ -252,7 +255,13 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
         return
 
-    cfg = CONFIGS[args.config]
+    cfg = dict(CONFIGS[args.config])
+    if args.precision and args.precision != cfg["precision"]:
+        if (args.precision == "fp32") != (cfg["precision"] == "fp32"):
+            print("bench.py: --precision switches between the bf16-I/O precisions only", file=sys.stderr)
+            sys.exit(2)
+        cfg["precision"] = args.precision
+        cfg["workload"] = cfg["workload"] + "_as_" + args.precision
     F, N, H, d, prec = cfg["F"], cfg["N"], cfg["H"], cfg["d"], cfg["precision"]
     p = vdn.PRECISIONS[prec]
     fp32 = prec == "fp32"
@@ -312,7 +321,7 @@ def main():
     # bf16 and fp8 layers run the readout and merge in the attention kernel, the
     # fp32 layer in its own pass
     run = [st for st, name in enumerate(vdn.STAGES)
-           if (name != "quant" or prec == "bf16_fp8qk") and (name != "readout" or fp32)
+           if (name != "quant" or prec in ("bf16_fp8qk", "fp8")) and (name != "readout" or fp32)
            and (name != "proj" or Dp > 0)]
 
     def new_pair():
@@ -352,12 +361,15 @@ def main():
         # q.k at the fp8 peak, p.v and W q at the bf16 peak: their time-weighted peak
         half = work["soft"] / 2
         peak = kflop / (half / PEAK_FP8_TFLOPS + (half + work["readout"]) / PEAK_BF16_TFLOPS)
+    elif prec == "fp8":
+        # q.k and p.v at the fp8 peak, W q at the bf16 peak
+        peak = kflop / (work["soft"] / PEAK_FP8_TFLOPS + work["readout"] / PEAK_BF16_TFLOPS)
     elif fp32:
         peak = PEAK_FP32_TFLOPS
     else:
         peak = PEAK_BF16_TFLOPS
     achieved = kflop / (attn_ms * 1e-3) / 1e12
-    traffic = measured_traffic(args.config) if (T == 0 and Dp == 0) else None
+    traffic = measured_traffic(args.config) if (T == 0 and Dp == 0 and not args.precision) else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                 "traffic_source": ("rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, calibrated on a copy, from "
@@ -409,7 +421,7 @@ def main():
                         "its cost is the attention stage with it minus without it, medians of interleaved runs"}
         del Sf, Sb, Os
 
-    dtype = {"fp32": "fp32", "bf16": "bf16", "bf16_fp8qk": "bf16+fp8e4m3(q.k)"}[prec]
+    dtype = {"fp32": "fp32", "bf16": "bf16", "bf16_fp8qk": "bf16+fp8e4m3(q.k)", "fp8": "bf16+fp8e4m3(q.k,p.v)"}[prec]
     result = {
         "metric": METRIC, "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": round(ms, 3), "higher_is_better": False,
