@@ -716,7 +716,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   const unsigned char* kbase = FP8 ? reinterpret_cast<const unsigned char*>(a.k8)
                                    : static_cast<const unsigned char*>(a.k);
   auto frame_of = [&](int slot) {
-    return it.mode == 0 ? it.k_f0 + slot : chunk_key_frame(slot, it.wf, it.we, F);
+    // The two forms of the lookup (and the two epilogue shapes below) make the
+    // compiler lay out the tile loop differently, and the attention kernel's speed
+    // and L2-miss traffic follow the layout; each path takes the combination
+    // measured fastest for it (same-box A/B: bf16 at the 768p workload 247.6 vs
+    // 252.4 ms, 255 vs 515 GB past L2; fp8 q.k at the long stream 425.7 vs 441.0 ms,
+    // 308 vs 807 GB; full fp8 340.3 vs 344.2 ms).
+    if constexpr (PREC == 2) return it.mode == 0 ? it.k_f0 + slot : chunk_key_frame_sel(slot, it.wf, it.we, F);
+    else return it.mode == 0 ? it.k_f0 + slot : chunk_key_frame(slot, it.wf, it.we, F);
   };
   // Per-lane byte offsets of this lane's 16-byte pieces inside a K tile (rows of
   // the token-major k tensor) and a V^T block; the tile base is wave-uniform.
@@ -1052,6 +1059,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   }
   const uint16_t* Wp = kargs->W;
   const bool lin = it.split < 0 && Wp != nullptr;    // workgroup-uniform
+  // fp8 paths: q rows as stored (the resident fragments are E4M3 codes); the
+  // fp8-q.k path loads them beside the W tile, the full-fp8 path at the readout
+  // (the shape measured faster for each, see frame_of)
+  constexpr bool EARLY_Q = PREC == 2;
+  bf16x8 q8r[EARLY_Q ? D / 16 : 1];
   if (lin) {
     const int chunk = it.q_tok0 / N / kChunk;      // chunk of the item's first (and every) row
     const uint16_t* wsrc = Wp + ((size_t)chunk * H + h) * (size_t)(D * D);
@@ -1065,6 +1077,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (lds_void_ptr)(smem + 1024 * (x * NW + w)), 16,
                                                (uint32_t)(row * 2 * D + 16 * c), 0, 0, 0);
     }
+    if constexpr (EARLY_Q) {
+      const uint16_t* qrow = static_cast<const uint16_t*>(kargs->q) + (size_t)(it.q_tok0 + qi) * rs + (size_t)h * D;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        q8r[s] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hf) : bf16x8{};
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -1076,7 +1094,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       constexpr int QS = D / 16;
       bf16x8 qr[QS];
       float us;
-      if constexpr (FP8) {
+      if constexpr (EARLY_Q) {
+#pragma unroll
+        for (int s = 0; s < QS; ++s) qr[s] = q8r[s];
+        us = 1.f;
+      } else if constexpr (FP8) {
         const uint16_t* q = static_cast<const uint16_t*>(a.q);
 #pragma unroll
         for (int s = 0; s < QS; ++s)
@@ -1122,7 +1144,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
     constexpr int QS = D / 16;
     bf16x8 qr[QS];
     float us;
-    if constexpr (FP8) {
+    if constexpr (EARLY_Q) {
+#pragma unroll
+      for (int s = 0; s < QS; ++s) qr[s] = q8r[s];
+      us = 1.f;
+    } else if constexpr (FP8) {
       const uint16_t* q = static_cast<const uint16_t*>(a.q);
 #pragma unroll
       for (int s = 0; s < QS; ++s)
@@ -1140,7 +1166,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       for (int s = 0; s < QS; ++s)
         acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(smem + (32 * db + j) * WP + 16 * (2 * s + hf)), qr[s], acc);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] = fmaf(acc[r], us, o[db][r] * inv);
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (EARLY_Q) o[db][r] = fmaf(o[db][r], inv, acc[r]);
+        else o[db][r] = fmaf(acc[r], us, o[db][r] * inv);
+      }
     }
     inv = 1.f;
   }
