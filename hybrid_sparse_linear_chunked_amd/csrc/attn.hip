@@ -801,6 +801,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   // MFMAs leave s - m and the exponent needs no VALU op; m is finite from the
   // start and the first tile sets it to that tile's maximum
   float m_run = 0.f, l_run = 0.f;
+  // full fp8: the row sums come from the matrix core, one more 64-deep MFMA per tile
+  // with an all-ones A operand, so they are the sums of the rounded probabilities
+  // that P.V uses (every element of lsum holds the lane's query's whole sum)
+  floatx16 lsum = floatx16{};
   floatx16 nm = floatx16{};      // -m in every element: the first Q.K^T accumulator input
   if constexpr (XI) {
     // start from the state after the extra tokens' keys (l on the first half-wave
@@ -928,6 +932,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
         if (!first) {
           const float alpha = __builtin_amdgcn_exp2f(-dm);
           l_run *= alpha;
+          if constexpr (Cfg::FP8V) lsum *= alpha;
 #pragma unroll
           for (int x = 0; x < NDB; ++x) o[x] *= alpha;
         }
@@ -950,11 +955,11 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       // for keys 32 kb + 8 (r / 4) + 4 hf + r % 4 (kb = 0, 1; r = 0..15), packed as
       // bytes 16 kb + r of its B operand; the vt8 layout puts the same keys at the
       // same bytes of the lane's V^T operand.  P is in (0, 2^kLazy], inside E4M3's
-      // range; the row sum takes the unrounded fp32 probabilities.
+      // range.  The row sums take the same rounded values (the all-ones MFMA into
+      // lsum), replacing 32 vector adds per tile with one MFMA.
       intx8 vf8[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) vf8[db] = Cfg::vfrag8(vbase, db, j, hf);
-      float psum = 0.f;
       intx8 pf;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -964,12 +969,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
         int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
         wd = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
         pf[t] = wd;
-        psum += (p0 + p1) + (p2 + p3);
       }
       lds_wait_all();
 #pragma unroll
       for (int db = 0; db < NDB; ++db) o[db] = mfma_fp8_scaled(vf8[db], pf, o[db], sv, 127);
-      l_run += psum;
+      constexpr int kOne = 0x38383838;      // E4M3 1.0 in every byte
+      lsum = mfma_fp8_scaled(intx8{kOne, kOne, kOne, kOne, kOne, kOne, kOne, kOne}, pf, lsum, 127, 127);
     } else {
     // ---- O^T += V^T P^T, one group of 16 keys per batch; the probabilities of
     // the next group are formed on the VALU while this group's MFMAs run, and
@@ -1019,7 +1024,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   }
 
   // ---- epilogue
-  const float l_tot = pair_sum(l_run);
+  const float l_tot = Cfg::FP8V ? lsum[0] : pair_sum(l_run);
   // Linear-branch readout and gated merge, fused (besthub article "VDN-H3
   // Generates 14-Second 768p Video ...", Hybrid Attention Architecture: the gated
   // linear output is added to the softmax output): every query row of a chunk
