@@ -67,7 +67,8 @@ int check_extra(int F, int N, int T, int prec) {
 
 // Workspace carving (byte offsets).
 struct Layout {
-  size_t vt = 0, vtx = 0, px = 0, G = 0, B = 0, Sf = 0, Sb = 0, W = 0, pO = 0, pml = 0, q8 = 0, k8 = 0, fexp = 0;
+  size_t vt = 0, vtx = 0, px = 0, G = 0, B = 0, Sf = 0, Sb = 0, W = 0, pO = 0, pml = 0, q8 = 0, k8 = 0, fexp = 0,
+         qctr = 0;
   size_t total = 0;
 };
 
@@ -98,6 +99,7 @@ Layout layout(int F, int N, int H, int d, int prec, int T = 0) {
   const size_t rows = na * N + static_cast<size_t>(T);      // split rows per head: anchors, extras
   L.pO = take(static_cast<size_t>(nsplit) * H * rows * d * 4);
   L.pml = take(static_cast<size_t>(nsplit) * H * rows * 2 * 4);
+  L.qctr = take(prec == VDN_PREC_FP32 ? 0 : 8 * 4);        // attention item-queue cursors
   if (prec >= VDN_PREC_BF16_FP8QK) {
     const size_t ntok = static_cast<size_t>(F) * N + T;
     L.q8 = take(ntok * H * d);
@@ -183,7 +185,7 @@ int run_softmax(const void* q, const void* k, const void* v, int F, int N, int H
   VDN_STAGE(VDN_STAGE_ATTN, st,
             vdn::launch_attn(kprec, q, k, v, ws.at<uint16_t>(L.vt), q8, k8, fexp, F, N, H, d, O,
                              ws.at<float>(L.pO), ws.at<float>(L.pml), W, T, ws.at<uint16_t>(L.vtx), split,
-                             ws.at<float>(L.px), st));
+                             ws.at<float>(L.px), prec == VDN_PREC_FP32 ? nullptr : ws.at<int>(L.qctr), st));
   VDN_STAGE(VDN_STAGE_COMBINE, st,
             vdn::launch_combine(prec == VDN_PREC_FP32 ? 0 : 1, ws.at<float>(L.pO), ws.at<float>(L.pml),
                                 F, N, T, H, d, O, split, st));

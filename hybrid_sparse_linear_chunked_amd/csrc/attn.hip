@@ -661,8 +661,22 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   // the item is wave-uniform; say so, so that tile bookkeeping stays in SGPRs
   int xs = -1;                 // with extra tokens: their slot in the key list
   Item it0;
-  if constexpr (XT) it0 = decode_item_x(a, &xs);
-  else it0 = decode_item(a);
+  if constexpr (XT) {
+    it0 = decode_item_x(a, &xs);
+  } else if (a.qctr != nullptr) {
+    // the item from the queues: one thread takes it, and the LDS word after the
+    // tile stages hands it to the other waves
+    int* slot = reinterpret_cast<int*>(smem + kLdsStages * Cfg::STAGE);
+    if (tid == 0) *slot = acquire_item(a);
+    __syncthreads();
+    const int pk = __builtin_amdgcn_readfirstlane(*slot);
+    if (pk < 0) return;      // every queue empty (the grid's spare workgroups)
+    const int M = a.na * a.qt_anchor * a.nsplit + a.tiles_per_head;
+    const int hh = pk / M;
+    it0 = decode_item_at(a, hh, pk - hh * M);
+  } else {
+    it0 = decode_item(a);
+  }
   const Item it = uniform_item(it0);
   const int xslot = XT ? __builtin_amdgcn_readfirstlane(xs) : -1;
   // the second wave of every SIMD issues first when both are ready: a fixed order
@@ -1271,6 +1285,12 @@ __global__ void fill_u32_kernel(uint32_t* p, int n, uint32_t value) {
   if (i < n) p[i] = value;
 }
 
+hipError_t launch_fill_u32(uint32_t* p, int n, uint32_t value, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n, value);
+  return hipGetLastError();
+}
+
 // grid (ceil(F*N / 1024), H), 256 threads: max |x| over 1024 tokens of head h.
 template <int D>
 __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ x, size_t ntok, int H,
@@ -1375,9 +1395,9 @@ void attn_split_plan(int F, int* nsplit, int* fs) {
 
 template <typename KernelFn>
 static hipError_t attn_launch(KernelFn fn, int lds, std::atomic<unsigned long long>* attr_done, AttnArgs a, hipStream_t st,
-                              int threads, int bq = 0) {
-  a.bq = bq > 0 ? bq : 32 * (threads / 64);
-  return attn_launch_items(fn, lds, attr_done, a, st, threads);
+                              int threads, bool queue = false) {
+  a.bq = 32 * (threads / 64);
+  return attn_launch_items(fn, lds, attr_done, a, st, threads, queue);
 }
 
 // fp32 I/O: the register-staged kernel; bf16 and fp8: the direct-to-LDS kernel
@@ -1388,12 +1408,13 @@ static hipError_t attn_f32(const AttnArgs& a, hipStream_t st) {
 }
 template <int D, int PREC>
 static hipError_t attn_lds(const AttnArgs& a, hipStream_t st, bool split) {
-  constexpr int lds = kLdsStages * LdsCfg<D, PREC>::STAGE;
+  // the tile stages, then one word that hands a queued item to every wave
+  constexpr int lds = kLdsStages * LdsCfg<D, PREC>::STAGE + 16;
   if constexpr (PREC == 3) {
     // fp8 P.V: the plain layer only (no extra tokens, no split output)
     if (split || a.T > 0) return hipErrorInvalidValue;
     static std::atomic<unsigned long long> done8{0};
-    return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, false>, lds, &done8, a, st, 64 * kLdsWaves);
+    return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, false>, lds, &done8, a, st, 64 * kLdsWaves, true);
   } else {
   if constexpr (D == 128) {
     // opt-in: the 64-queries-per-wave kernel (half the LDS reads per MFMA, one
@@ -1402,7 +1423,7 @@ static hipError_t attn_lds(const AttnArgs& a, hipStream_t st, bool split) {
   }
   if (split) {   // (no extra tokens in this form)
     static std::atomic<unsigned long long> done_s{0};
-    return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, true>, lds, &done_s, a, st, 64 * kLdsWaves);
+    return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, true>, lds, &done_s, a, st, 64 * kLdsWaves, true);
   }
   if (a.T > 0) {
     // the split items, and the chunk items over the extra tokens' keys (state to
@@ -1416,18 +1437,19 @@ static hipError_t attn_lds(const AttnArgs& a, hipStream_t st, bool split) {
     b.T = 0;
     b.nbx = 0;
     return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, false, true>, lds, &done_i, b, st,
-                       64 * kLdsWaves);
+                       64 * kLdsWaves, true);
   }
   static std::atomic<unsigned long long> done{0};
-  return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, false>, lds, &done, a, st, 64 * kLdsWaves);
+  return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, false>, lds, &done, a, st, 64 * kLdsWaves, true);
   }
 }
 
 hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, const uint16_t* vt,
                        const uint8_t* q8, const uint8_t* k8, const int* fexp, int F, int N, int H,
                        int D, void* O, float* part_O, float* part_ml, const uint16_t* W,
-                       int T, const uint16_t* vtx, int split, float* px, hipStream_t st) {
+                       int T, const uint16_t* vtx, int split, float* px, int* qctr, hipStream_t st) {
   AttnArgs a;
+  a.qctr = qctr;
   a.q = q; a.k = k; a.v = v; a.vt = vt; a.q8 = q8; a.k8 = k8; a.fexp = fexp;
   a.O = O; a.part_O = part_O; a.part_ml = part_ml;
   a.W = W;

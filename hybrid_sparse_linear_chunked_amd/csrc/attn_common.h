@@ -4,9 +4,11 @@
 // of the direct-load kernels.
 #pragma once
 
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 #include <type_traits>
+#include <vector>
 
 #include "common.h"
 #include "kernels.h"
@@ -49,6 +51,13 @@ struct AttnArgs {
   // extra tokens' keys, [H][F*N][D + 4] (o unnormalised, m, l, 2 pad), written by the
   // extra-token instantiation and the start of the video pass
   float* px;
+  // Item queues (attn_lds_kernel without extra tokens; null: the static map of
+  // decode_item).  Queue x holds, head after head, the items [run[x], run[x+1]) of
+  // every head (contiguous runs of about equal cost); qctr[x] is its cursor, zero
+  // at launch.  A workgroup takes the next item of its own XCD's queue, or, once
+  // that is empty, of the next non-empty queue.
+  int* qctr;
+  int run[9];
 };
 
 constexpr int BQ = 128;   // queries per work item of attn_kernel (4 waves x 32)
@@ -156,20 +165,11 @@ struct Item {
   int k_f0, wf, we, nslots;
 };
 
-// Work item of this workgroup (same numbering as attn_kernel).
-__device__ inline Item decode_item(const AttnArgs& a) {
+// Item li of head hh (items per head: the anchor items, then the chunk items).
+__device__ inline Item decode_item_at(const AttnArgs& a, int hh, int li) {
   Item it;
   const int F = a.F, N = a.N;
-  // Blocks go out head by head (all XCDs stream one head's K / V^T at a time,
-  // which the last-level cache holds); inside a head, the blocks one XCD receives
-  // (every 8th, as the dispatcher deals them round-robin) take a contiguous run of
-  // the head's items, so the items that share key frames share that XCD's L2.
   const int na_h = a.na * a.qt_anchor * a.nsplit;        // anchor items per head
-  const int M = na_h + a.tiles_per_head;                 // items per head
-  const int b = blockIdx.x;
-  const int hh = b / M, p = b - hh * M;
-  const int q8 = M >> 3, m8 = M & 7, r = p & 7;
-  const int li = r * q8 + min(r, m8) + (p >> 3);         // item of head hh
   it.wf = it.we = it.k_f0 = 0;
   if (li < na_h) {
     int rr = li;
@@ -208,6 +208,40 @@ __device__ inline Item decode_item(const AttnArgs& a) {
   return it;
 }
 
+// Work item of this workgroup from its block index (same numbering as attn_kernel).
+// Blocks go out head by head (all XCDs stream one head's K / V^T at a time, which
+// the last-level cache holds); inside a head, the blocks one XCD receives (every
+// 8th, as the dispatcher deals them round-robin) take a contiguous run of the
+// head's items, so the items that share key frames share that XCD's L2.
+__device__ inline Item decode_item(const AttnArgs& a) {
+  const int M = a.na * a.qt_anchor * a.nsplit + a.tiles_per_head;   // items per head
+  const int b = blockIdx.x;
+  const int hh = b / M, p = b - hh * M;
+  const int q8 = M >> 3, m8 = M & 7, r = p & 7;
+  return decode_item_at(a, hh, r * q8 + min(r, m8) + (p >> 3));
+}
+
+// Next item from the queues (one thread per workgroup): hh * M + li, or -1 when
+// every queue is empty.  The XCD a workgroup runs on only picks the queue it tries
+// first, so every item is taken exactly once whatever the dispatcher does, as long
+// as the grid has at least as many workgroups as items.
+__device__ inline int acquire_item(const AttnArgs& a) {
+  const int M = a.na * a.qt_anchor * a.nsplit + a.tiles_per_head;
+  const int x = __builtin_amdgcn_s_getreg((15 << 11) | 20) & 7;   // HW_REG_XCC_ID
+  for (int k = 0; k < 8; ++k) {
+    const int y = (x + k) & 7;
+    const int rl = a.run[y + 1] - a.run[y];
+    const int n = rl * a.H;
+    if (n == 0 || __hip_atomic_load(a.qctr + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
+    const int i = __hip_atomic_fetch_add(a.qctr + y, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (i < n) {
+      const int hh = i / rl;
+      return hh * M + a.run[y] + (i - hh * rl);
+    }
+  }
+  return -1;
+}
+
 
 // An item with every field read from the first lane: it is the same in every
 // lane, and this lets the compiler keep it and what derives from it in SGPRs.
@@ -239,16 +273,65 @@ inline void attn_items(AttnArgs& a) {
   a.tiles_per_head = tph;
 }
 
-// One workgroup per work item of a.bq query rows (a.bq set by the caller).
+// Item queues: the 8 runs of every head's items, cut where the running cost (key
+// tiles, plus about 7 tiles' worth for an item's prologue and epilogue) crosses
+// k/8 of the head's total.
+inline void attn_queue_plan(AttnArgs& a) {
+  const int nb = (a.N + BK - 1) / BK;
+  const int na_h = a.na * a.qt_anchor * a.nsplit;
+  std::vector<long long> cost;
+  for (int li = 0; li < na_h; ++li) {
+    const int split = li / a.qt_anchor / a.na;
+    const int k0 = split * a.fs;
+    cost.push_back((long long)(std::min(a.F, k0 + a.fs) - k0) * nb + 7);
+  }
+  for (int c = 0; c < num_chunks(a.F); ++c) {
+    const int nf = nq_end(c, a.F) - nq_first(c);
+    if (nf <= 0) continue;
+    const int t = (int)(((long long)nf * a.N + a.bq - 1) / a.bq);
+    const int wf = win_first(c), we = win_end(c, a.F);
+    const int nsl = (wf > 0 ? 1 : 0) + (we - wf) + (we < a.F ? 1 : 0);
+    for (int r = 0; r < t; ++r) cost.push_back((long long)nsl * nb + 7);
+  }
+  long long total = 0;
+  for (long long c : cost) total += c;
+  const int M = (int)cost.size();
+  a.run[0] = 0;
+  long long acc = 0;
+  int li = 0;
+  for (int k = 1; k < 8; ++k) {
+    while (li < M && 8 * (acc + cost[li] / 2) < k * total) acc += cost[li++];
+    a.run[k] = li;
+  }
+  a.run[8] = M;
+}
+
+// The kernels' fill (attn.hip)
+hipError_t launch_fill_u32(uint32_t* p, int n, uint32_t value, hipStream_t st);
+
+// One workgroup per work item of a.bq query rows (a.bq set by the caller); with
+// queue, items come from the queues of a.qctr (cleared here), and the grid has
+// an eighth more workgroups than items so that an XCD that runs ahead can take
+// items from the others' queues (the extra workgroups find every queue empty and
+// return).
 template <typename KernelFn>
 inline hipError_t attn_launch_items(KernelFn fn, int lds, std::atomic<unsigned long long>* attr_done, AttnArgs a,
-                                    hipStream_t st, int threads) {
+                                    hipStream_t st, int threads, bool queue = false) {
   attn_items(a);
   hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(fn), lds, attr_done);
   if (e != hipSuccess) return e;
   const int nitems = a.n_anchor_items + a.H * a.tiles_per_head;
   if (nitems == 0) return hipSuccess;
-  hipLaunchKernelGGL(fn, dim3(nitems), dim3(threads), lds, st, a);
+  int grid = nitems;
+  if (queue && a.qctr != nullptr) {
+    attn_queue_plan(a);
+    e = launch_fill_u32(reinterpret_cast<uint32_t*>(a.qctr), 8, 0u, st);
+    if (e != hipSuccess) return e;
+    grid = nitems + (nitems / 8 + 64 + 7) / 8 * 8;
+  } else {
+    a.qctr = nullptr;
+  }
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(threads), lds, st, a);
   return hipGetLastError();
 }
 

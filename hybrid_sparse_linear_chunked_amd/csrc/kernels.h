@@ -35,10 +35,12 @@ hipError_t launch_proj(const uint16_t* A, const uint16_t* B, int M, int N, int K
 hipError_t launch_prep(const uint16_t* k, const uint16_t* v, int F, int N, int H, int D,
                        uint16_t* vt, float* G, float* B, int grams, hipStream_t st, uint8_t* vt8 = nullptr,
                        const int* vexp = nullptr);
+// qctr: 8 ints of scratch for the bf16 / fp8 kernel's item queues (cleared by the
+// launch), or null for the static block -> item map
 hipError_t launch_attn(int prec, const void* q, const void* k, const void* v, const uint16_t* vt,
                        const uint8_t* q8, const uint8_t* k8, const int* fexp, int F, int N, int H,
                        int D, void* O, float* part_O, float* part_ml, const uint16_t* W,
-                       int T, const uint16_t* vtx, int split, float* px, hipStream_t st);
+                       int T, const uint16_t* vtx, int split, float* px, int* qctr, hipStream_t st);
 hipError_t launch_combine(int prec, const float* part_O, const float* part_ml, int F, int N, int T,
                           int H, int D, void* O, int split, hipStream_t st);
 // The softmax temperature in base-2 units, log2(e) / sqrt(d), in fp32 (the bf16
