@@ -399,7 +399,7 @@ int vdn_hybrid_attn_proj(const void* q, const void* k, const void* v, const floa
     return s;
   VDN_STAGE(VDN_STAGE_PROJ, st,
             vdn::launch_proj(Acat, static_cast<const uint16_t*>(Wp), F * N, D, 2 * H * d, static_cast<uint16_t*>(Y),
-                             st));
+                             st, ws.at<int>(L.qctr)));
   return VDN_OK;
 }
 

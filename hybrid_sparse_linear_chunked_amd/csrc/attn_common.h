@@ -306,9 +306,6 @@ inline void attn_queue_plan(AttnArgs& a) {
   a.run[8] = M;
 }
 
-// The kernels' fill (attn.hip)
-hipError_t launch_fill_u32(uint32_t* p, int n, uint32_t value, hipStream_t st);
-
 // One workgroup per work item of a.bq query rows (a.bq set by the caller); with
 // queue, items come from the queues of a.qctr (cleared here), and the grid has
 // an eighth more workgroups than items so that an XCD that runs ahead can take

@@ -27,7 +27,12 @@ inline hipError_t set_max_lds_once(const void* fn, int lds, std::atomic<unsigned
 }
 
 // proj.hip: Y[M, N] = A[M, K] B[N, K]^T (bf16, fp32 accumulation); K % 64 == 0, N % 8 == 0
-hipError_t launch_proj(const uint16_t* A, const uint16_t* B, int M, int N, int K, uint16_t* Y, hipStream_t st);
+// qctr: 8 ints of scratch for the tile queues (cleared by the launch), or null for
+// the static block -> tile map
+hipError_t launch_proj(const uint16_t* A, const uint16_t* B, int M, int N, int K, uint16_t* Y, hipStream_t st,
+                       int* qctr = nullptr);
+// p[0, n) = value (a kernel, so that it can sit in a captured graph)
+hipError_t launch_fill_u32(uint32_t* p, int n, uint32_t value, hipStream_t st);
 
 // attn.hip
 // vt8 (optional): V^T as E4M3 codes in the vt8 layout, with scale exponents vexp [H],

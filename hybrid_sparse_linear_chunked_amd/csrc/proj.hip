@@ -40,19 +40,46 @@ constexpr int PJ_LX = (PJ_LOADS + PJ_NW - 1) / PJ_NW;  // per wave (the last par
 constexpr int PJ_LDS = 2 * PJ_STAGE;                   // 144 KiB
 
 // (the launcher checks K % 64 == 0, N % 8 == 0, M, N, K > 0 and 2*K*256 < 2^32)
+// Next tile from the queues (one thread per workgroup), or -1 when all are empty:
+// queue x holds the x-th of 8 contiguous runs of the tile list, qctr[x] its cursor
+// (zero at launch).  A workgroup takes from its own XCD's queue first, then from
+// the next non-empty one, so an XCD that runs ahead takes tiles from the others.
+__device__ inline int acquire_tile(int* qctr, int T) {
+  const int q8 = T >> 3, m8 = T & 7;
+  const int x = __builtin_amdgcn_s_getreg((15 << 11) | 20) & 7;   // HW_REG_XCC_ID
+  for (int k = 0; k < 8; ++k) {
+    const int y = (x + k) & 7;
+    const int n = q8 + (y < m8 ? 1 : 0);
+    if (n == 0 || __hip_atomic_load(qctr + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) continue;
+    const int i = __hip_atomic_fetch_add(qctr + y, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (i < n) return y * q8 + min(y, m8) + i;
+  }
+  return -1;
+}
+
 __global__ __launch_bounds__(64 * PJ_NW, 1) void proj_kernel(const uint16_t* __restrict__ A,
                                                              const uint16_t* __restrict__ B, int M, int N,
-                                                             int K, uint16_t* __restrict__ Y) {
+                                                             int K, uint16_t* __restrict__ Y, int* qctr) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, hf = lane >> 5;
 
-  // this workgroup's tile: the blocks one XCD receives (every 8th) take a
-  // contiguous run of the tile list
+  // this workgroup's tile: the XCDs take contiguous runs of the tile list, from
+  // the queues when qctr is set (the LDS word after the stages hands the tile to
+  // every wave), else the blocks one XCD receives (every 8th) take the run
   const int tn_count = (N + PJ_TN - 1) / PJ_TN, tm_count = (M + PJ_TM - 1) / PJ_TM;
   const int T = tm_count * tn_count;
-  const int b = blockIdx.x, q8 = T >> 3, m8 = T & 7, r = b & 7;
-  const int t = r * q8 + min(r, m8) + (b >> 3);
+  int t;
+  if (qctr != nullptr) {
+    int* slot = reinterpret_cast<int*>(smem + PJ_LDS);
+    if (tid == 0) *slot = acquire_tile(qctr, T);
+    __syncthreads();
+    t = __builtin_amdgcn_readfirstlane(*slot);
+    if (t < 0) return;       // every queue empty (the grid's spare workgroups)
+  } else {
+    const int b = blockIdx.x, q8 = T >> 3, m8 = T & 7, r = b & 7;
+    t = r * q8 + min(r, m8) + (b >> 3);
+  }
   // grouped order: G M tiles x all N tiles per group, m fastest inside a group
   // (the last group takes the M tiles left over)
   constexpr int G = 4;
@@ -171,15 +198,26 @@ __global__ __launch_bounds__(64 * PJ_NW, 1) void proj_kernel(const uint16_t* __r
 
 }  // namespace
 
-hipError_t launch_proj(const uint16_t* A, const uint16_t* B, int M, int N, int K, uint16_t* Y, hipStream_t st) {
+hipError_t launch_proj(const uint16_t* A, const uint16_t* B, int M, int N, int K, uint16_t* Y, hipStream_t st,
+                       int* qctr) {
   if (M <= 0 || N <= 0 || K <= 0 || K % PJ_TK != 0 || N % 8 != 0) return hipErrorInvalidValue;
   if ((long long)PJ_TM * 2 * K >= (1LL << 32)) return hipErrorInvalidValue;   // 32-bit buffer offsets
+  // the stages, then one word that hands a queued tile to every wave
+  constexpr int lds = PJ_LDS + 16;
   static std::atomic<unsigned long long> attr_done{0};
-  hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(&proj_kernel), PJ_LDS, &attr_done);
+  hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(&proj_kernel), lds, &attr_done);
   if (e != hipSuccess) return e;
   const long long tiles = (long long)((M + PJ_TM - 1) / PJ_TM) * ((N + PJ_TN - 1) / PJ_TN);
-  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(proj_kernel, dim3((unsigned)tiles), dim3(64 * PJ_NW), PJ_LDS, st, A, B, M, N, K, Y);
+  if (tiles > 0x7fffffff - (0x7fffffff >> 3) - 128) return hipErrorInvalidValue;
+  long long grid = tiles;
+  if (qctr != nullptr) {
+    // an eighth more workgroups than tiles: an XCD that runs ahead can take tiles
+    // from the others' queues; the spare workgroups find every queue empty
+    e = launch_fill_u32(reinterpret_cast<uint32_t*>(qctr), 8, 0u, st);
+    if (e != hipSuccess) return e;
+    grid = tiles + (tiles / 8 + 64 + 7) / 8 * 8;
+  }
+  hipLaunchKernelGGL(proj_kernel, dim3((unsigned)grid), dim3(64 * PJ_NW), lds, st, A, B, M, N, K, Y, qctr);
   return hipGetLastError();
 }
 
