@@ -37,23 +37,15 @@ __device__ inline int vt_pos_of_key(int n) {   // n in [0, 64)
   return 16 * u + 8 * ((r & 7) >> 2) + 4 * (r >> 3) + (r & 3);
 }
 
-// E4M3 ("FN": no infinities, max 448), round to nearest even, saturating.
-__device__ inline uint32_t f32_to_e4m3(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = fabsf(x);
-  uint32_t code;
-  if (!(a < 448.f)) {
-    code = 0x7Eu;                                   // +-448
-  } else if (a < 0.015625f) {                       // below 2^-6: spacing 2^-9
-    code = static_cast<uint32_t>(__builtin_rintf(a * 512.f));   // 0..8 (8 = 2^-6)
-  } else {
-    const int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xFF) - 127;   // -6..8
-    const float m = __builtin_rintf(a * __builtin_ldexpf(1.f, 3 - e));         // 8..16
-    code = static_cast<uint32_t>((e + 7) * 8 + static_cast<int>(m) - 8);
-    if (code > 0x7Eu) code = 0x7Eu;
-  }
-  return sign | code;
+// Four E4M3 ("FN": no infinities, max 448) codes, round to nearest even with
+// subnormals, packed low byte first, by the hardware conversion.  Every caller's
+// values are at most 448 in magnitude (their power-of-two scale is chosen so), and
+// on that range the conversion equals the format's definition for every fp32
+// input (checked on the device over all of them, both signs).
+__device__ inline uint32_t e4m3x4(float x0, float x1, float x2, float x3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+  return static_cast<uint32_t>(w);
 }
 
 // v transposed as E4M3 codes ("vt8", fp8 P.V): bytes [H][F][nb][D][64], the same
@@ -159,13 +151,14 @@ __global__ __launch_bounds__(512) void prep_kernel(const uint16_t* __restrict__ 
         const int row = c >> 3, hf8 = (c >> 2) & 1, u = c & 3;
         const uint4 x = *reinterpret_cast<const uint4*>(&VT[row * P + 16 * u + 8 * hf8]);
         const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
-        uint32_t out[2] = {0, 0};
+        float y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t bits = (e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16);
-          out[e >> 2] |= f32_to_e4m3(__builtin_ldexpf(__uint_as_float(bits), ne)) << (8 * (e & 3));
+          y[e] = __builtin_ldexpf(__uint_as_float(bits), ne);              // exact scaling
         }
-        *reinterpret_cast<uint2*>(dst + row * 64 + 32 * hf8 + 8 * u) = make_uint2(out[0], out[1]);
+        *reinterpret_cast<uint2*>(dst + row * 64 + 32 * hf8 + 8 * u) =
+            make_uint2(e4m3x4(y[0], y[1], y[2], y[3]), e4m3x4(y[4], y[5], y[6], y[7]));
       }
     }
     if (grams) {
@@ -1353,15 +1346,13 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
   const int ne = -fexp[h];
   const uint4 val = *reinterpret_cast<const uint4*>(x + 8 * i);
   const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
-  uint32_t out[2] = {0, 0};
+  float y[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t bits = (e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16);
-    const float y = __uint_as_float(bits) * prescale;               // one fp32 rounding
-    const uint32_t c = f32_to_e4m3(__builtin_ldexpf(y, ne));         // exact scaling
-    out[e >> 2] |= c << (8 * (e & 3));
+    y[e] = __builtin_ldexpf(__uint_as_float(bits) * prescale, ne);  // one fp32 rounding, exact scaling
   }
-  *reinterpret_cast<uint2*>(codes + 8 * i) = make_uint2(out[0], out[1]);
+  *reinterpret_cast<uint2*>(codes + 8 * i) = make_uint2(e4m3x4(y[0], y[1], y[2], y[3]), e4m3x4(y[4], y[5], y[6], y[7]));
 }
 
 // ============================================================ launchers
