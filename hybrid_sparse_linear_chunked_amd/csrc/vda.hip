@@ -71,172 +71,245 @@ __global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__
 }
 
 // ============================================================ per-frame affine maps
-// grid (F-2, H), FACTOR_THREADS threads (9 waves; two workgroups per CU, 4-5
-// waves per SIMD hide the latency of the serial column steps); frame t =
+// grid (F-2, H), 512 threads (8 waves; two workgroups per CU); frame t =
 // blockIdx.x + 1.
 // In:  G = K K^T, B = V K^T of frame t.   Out (in place): G <- M = A^-1,
 // B <- C = beta B M, with A = I + beta G.
-//   1. Cholesky A = L L^T, right-looking, and in the same column steps Y = L^-1
-//      by right-looking forward substitution on the identity.  Only lower
-//      triangles matter (A is symmetric, Y lower triangular), so thread i owns one
-//      RB x RB block (bi, bj), bi >= bj, of the 32 x 32 block grid, of A and of Y
-//      (528 blocks), in registers; step j broadcasts column j of A and row j of Y
-//      through LDS, one barrier per step.  With d = A_jj (A after j steps),
-//      L_rj = A_rj / sqrt(d) and row j of Y is final once scaled by 1 / sqrt(d), so
-//      both rank-1 updates take the broadcast values times 1 / d, and L is never
-//      stored.
-//   2. M = Y^T Y with fp32 MFMA (32x32x2) from LDS; M goes to G and, in LDS, over Y.
-//   3. C = beta B M with B read from global memory and M from LDS.
-constexpr int FACTOR_TG = 32;                                        // block grid side
-constexpr int FACTOR_NL = FACTOR_TG * (FACTOR_TG + 1) / 2;           // lower-triangle blocks
-constexpr int FACTOR_THREADS = (FACTOR_NL + 63) / 64 * 64;
+// The matrix lives in LDS (fp32, pitch D + 1) in 32 x 32 blocks, NB = D / 32 per side.
+//   1. Blocked Cholesky A = L L^T, right-looking, with T_k = L_kk^-1 in place of the
+//      diagonal block: for k = 0 .. NB-1,
+//        - one wave turns the diagonal block A_kk into T_k (a column step at a time,
+//          32 steps, no workgroup barrier; L_kk itself is never needed);
+//        - L_ik = A_ik T_k^T for i > k (in place), and U_kj = T_k L_kj for j < k (in
+//          place of L_kj, which no later step reads);
+//        - A_ij -= L_ik L_jk^T for NB > i >= j > k.
+//   2. Y = L^-1 by blocks: Y_kk = T_k, Y_ik = -sum_{j=k}^{i-1} U_ij Y_jk (i > k), in
+//      order of i - k; Y_ik is stored transposed in the free upper block (k, i).
+//   3. M = Y^T Y, block (a, b) = sum over R >= max(a, b) of Y_Ra^T Y_Rb; M goes to G
+//      and, in LDS, over A.
+//   4. C = beta B M with B read from global memory and M from LDS.
+// Every block product is 16 fp32 MFMAs (32x32x2); a wave owns whole blocks.
+constexpr int FACTOR_THREADS = 512;
+constexpr int FACTOR_NW = FACTOR_THREADS / 64;
+
+// acc += X Z over a 32-deep reduction, X[r][m] = xp[r * xr + m * xm], Z[m][c] =
+// zp[m * zm + c * zc] (lane j: row / column j, half hf: odd or even m)
+__device__ inline floatx16 block_mma(floatx16 acc, const float* xp, int xr, int xm, const float* zp, int zm, int zc,
+                                     int j, int hf) {
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int m = 2 * s + hf;
+    acc = mfma_f32(xp[j * xr + m * xm], zp[m * zm + j * zc], acc);
+  }
+  return acc;
+}
+// element r of a 32 x 32 accumulator is row 8 (r / 4) + 4 hf + r % 4, column j
+__device__ inline int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
+
+// Lanes of one wave exchanging values through LDS: the stores before this point
+// are visible to every lane's loads after it (LDS serves a wave's instructions in
+// order; the fences keep the compiler from moving or forwarding the accesses
+// across it, which per-lane program order alone would allow).
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+// One wave: the 32 x 32 diagonal block at Ab (pitch LP; lower triangle read) is
+// replaced by T = L^-1, L its Cholesky factor (zeros above the diagonal).  Lane
+// (i, hh) holds row i, columns 16 hh .. 16 hh + 15 of the block and of T; step p
+// broadcasts column p of the block and row p of T through cb / rb (in-order LDS
+// within the wave).  As in a right-looking step with d = A_pp (after p steps):
+// L_ip = A_ip / sqrt(d), so both rank-1 updates take the column times 1 / d, and
+// row p of T is final once scaled by 1 / sqrt(d).
+template <int LP>
+__device__ inline void diag_inverse_factor(float* Ab, float* cb, float* rb, int lane) {
+  const int i = lane & 31, hh = lane >> 5;
+  float a[16], y[16];
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    a[x] = Ab[i * LP + 16 * hh + x];
+    y[x] = (16 * hh + x == i) ? 1.f : 0.f;
+  }
+#pragma unroll
+  for (int p = 0; p < 32; ++p) {
+    if (hh == (p >> 4)) cb[i] = a[p & 15];
+    if (i == p) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) rb[16 * hh + x] = y[x];
+    }
+    wave_lds_sync();
+    // the lane's 16 entries of the broadcast column and row, read together
+    float cv[16], rv[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 c4 = *reinterpret_cast<const float4*>(cb + 16 * hh + 4 * q);
+      const float4 r4 = *reinterpret_cast<const float4*>(rb + 16 * hh + 4 * q);
+      cv[4 * q] = c4.x; cv[4 * q + 1] = c4.y; cv[4 * q + 2] = c4.z; cv[4 * q + 3] = c4.w;
+      rv[4 * q] = r4.x; rv[4 * q + 1] = r4.y; rv[4 * q + 2] = r4.z; rv[4 * q + 3] = r4.w;
+    }
+    const float d = cb[p];                       // the pivot, >= 1 (A = I + beta G)
+    const float inv_d = __builtin_amdgcn_rcpf(d);
+    const float rsq = __builtin_amdgcn_rsqf(d);
+    const float f = cb[i] * inv_d;
+    if (i > p) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        if (16 * hh + x > p) a[x] -= f * cv[x];
+        y[x] -= f * rv[x];
+      }
+    } else if (i == p) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) y[x] *= rsq;
+    }
+    wave_lds_sync();   // every lane's reads of this step before the next step's stores
+  }
+#pragma unroll
+  for (int x = 0; x < 16; ++x) Ab[i * LP + 16 * hh + x] = y[x];
+}
+
 template <int D>
-__global__ __launch_bounds__(FACTOR_THREADS, 2)
+__global__ __launch_bounds__(FACTOR_THREADS, 4)
 void factor_kernel(float* __restrict__ G, float* __restrict__ Bm, const float* __restrict__ beta, int F, int H) {
-  constexpr int TG = FACTOR_TG;
-  constexpr int NT = FACTOR_THREADS;
-  constexpr int NWV = NT / 64;
-  constexpr int RB = D / TG;
-  constexpr int LP = D + 1;
   constexpr int NB = D / 32;
+  constexpr int LP = D + 1;
+  constexpr int NW = FACTOR_NW;
   constexpr int NBLK = NB * NB;
-  constexpr int PER_WAVE = (NBLK + NWV - 1) / NWV;
+  constexpr int PER_WAVE = (NBLK + NW - 1) / NW;
   extern __shared__ float sm[];
-  float* Xs = sm;                 // [D][LP]: Y, later M
-  float* cbuf = Xs + D * LP;      // [2][D]: pivot column of A
-  float* rbuf = cbuf + 2 * D;     // [2][D]: pivot row of Y, before its scaling
+  float* As = sm;                 // [D][LP]: A, then L / U and T_k, then Y; then M
+  float* cb = As + D * LP;        // [32] column broadcast of the diagonal steps
+  float* rb = cb + 32;            // [32] row broadcast
+  auto blk = [&](int r, int c) { return As + 32 * r * LP + 32 * c; };
 
   const int t = blockIdx.x + 1, h = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, j = lane & 31, hf = lane >> 5;
-  // block (bi, bj) of this thread: tid = bi (bi + 1) / 2 + bj, 0 <= bj <= bi
-  const bool owns = tid < FACTOR_NL;
-  int bi = (int)((sqrtf(8.f * tid + 1.f) - 1.f) * 0.5f);
-  while (bi * (bi + 1) / 2 > tid) --bi;
-  while ((bi + 1) * (bi + 2) / 2 <= tid) ++bi;
-  const int bj = tid - bi * (bi + 1) / 2;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31, hf = lane >> 5;
   const float b = beta[(size_t)t * H + h];
   float* Gp = G + ((size_t)t * H + h) * D * D;
   float* Bp = Bm + ((size_t)t * H + h) * D * D;
 
-  float a[RB][RB], y[RB][RB];
-#pragma unroll
-  for (int ii = 0; ii < RB; ++ii)
-#pragma unroll
-    for (int kk = 0; kk < RB; ++kk) {
-      const int r = bi * RB + ii, c = bj * RB + kk;
-      a[ii][kk] = owns ? b * Gp[r * D + c] + (r == c ? 1.f : 0.f) : 0.f;
-      y[ii][kk] = r == c ? 1.f : 0.f;
-    }
-  for (int x = tid; x < D * LP; x += NT) Xs[x] = 0.f;   // Y's upper triangle stays zero
-
-  // ---- 1. Cholesky and L^-1, one column step at a time
-  for (int jb = 0; jb < TG; ++jb) {
-#pragma unroll
-    for (int jr = 0; jr < RB; ++jr) {
-      const int jj = jb * RB + jr;
-      float* cb = cbuf + (jj & 1) * D;
-      float* rv = rbuf + (jj & 1) * D;
-      if (owns && bj == jb) {
-#pragma unroll
-        for (int ii = 0; ii < RB; ++ii) cb[bi * RB + ii] = a[ii][jr];
-      }
-      if (owns && bi == jb) {
-#pragma unroll
-        for (int kk = 0; kk < RB; ++kk) rv[bj * RB + kk] = y[jr][kk];
-      }
-      __syncthreads();
-      const float dj = cb[jj];
-      const float inv_d = 1.f / dj;
-      const float rsq = 1.f / sqrtf(dj);
-      if (owns && bi >= jb) {
-        float cr[RB], cc[RB], yr[RB];
-#pragma unroll
-        for (int x = 0; x < RB; ++x) {
-          cr[x] = cb[bi * RB + x] * inv_d;
-          cc[x] = cb[bj * RB + x];
-          yr[x] = bj <= jb ? rv[bj * RB + x] : 0.f;
-        }
-#pragma unroll
-        for (int ii = 0; ii < RB; ++ii) {
-          const int r = bi * RB + ii;
-          if (r > jj) {
-#pragma unroll
-            for (int kk = 0; kk < RB; ++kk) {
-              if (bj * RB + kk > jj) a[ii][kk] -= cr[ii] * cc[kk];
-              y[ii][kk] -= cr[ii] * yr[kk];
-            }
-          }
-        }
-        if (bi == jb) {
-#pragma unroll
-          for (int kk = 0; kk < RB; ++kk) y[jr][kk] *= rsq;
-        }
-      }
-    }
-  }
-  if (owns) {
-#pragma unroll
-    for (int ii = 0; ii < RB; ++ii)
-#pragma unroll
-      for (int kk = 0; kk < RB; ++kk) Xs[(bi * RB + ii) * LP + bj * RB + kk] = y[ii][kk];
+  for (int e = tid; e < D * D; e += FACTOR_THREADS) {
+    const int r = e / D, c = e - r * D;
+    As[r * LP + c] = b * Gp[e] + (r == c ? 1.f : 0.f);
   }
   __syncthreads();
 
-  // ---- 2. M = Y^T Y  (M[a][b] = sum_k Y[k][a] Y[k][b])
-  floatx16 acc[PER_WAVE];
+  // ---- 1. blocked Cholesky, T_k in the diagonal blocks
+  for (int k = 0; k < NB; ++k) {
+    if (w == 0) diag_inverse_factor<LP>(blk(k, k), cb, rb, lane);
+    __syncthreads();
+    // tasks 0 .. k-1: U_kj = T_k L_kj; tasks k .. NB-2: L_ik = A_ik T_k^T, i = task + 1
+    for (int task = w; task < NB - 1; task += NW) {
+      floatx16 acc = floatx16{};
+      float* out;
+      if (task < k) {
+        out = blk(k, task);
+        acc = block_mma(acc, blk(k, k), LP, 1, out, LP, 1, j, hf);
+      } else {
+        out = blk(task + 1, k);
+        acc = block_mma(acc, out, LP, 1, blk(k, k), 1, LP, j, hf);
+      }
+      // (the wave's own reads of `out` are complete: every MFMA above consumed them)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) out[acc_row(r, hf) * LP + j] = acc[r];
+    }
+    __syncthreads();
+    // A_ij -= L_ik L_jk^T, NB > i >= j > k; task = pair index in row-major order
+    const int m = NB - 1 - k;
+    for (int task = w; task < m * (m + 1) / 2; task += NW) {
+      int i = 0;
+      while ((i + 1) * (i + 2) / 2 <= task) ++i;
+      const int jj = task - i * (i + 1) / 2;
+      float* out = blk(k + 1 + i, k + 1 + jj);
+      floatx16 acc = floatx16{};
+      acc = block_mma(acc, blk(k + 1 + i, k), LP, 1, blk(k + 1 + jj, k), 1, LP, j, hf);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) out[acc_row(r, hf) * LP + j] -= acc[r];
+    }
+    __syncthreads();
+  }
+
+  // ---- 2. Y = L^-1: Y_ik (i = k + dl) = -sum_{jj=k}^{i-1} U_i,jj Y_jj,k, stored
+  // transposed in block (k, i); Y_kk = T_k sits in the diagonal block as [row][col]
+  for (int dl = 1; dl < NB; ++dl) {
+    for (int k = w; k < NB - dl; k += NW) {
+      const int i = k + dl;
+      floatx16 acc = floatx16{};
+      acc = block_mma(acc, blk(i, k), LP, 1, blk(k, k), LP, 1, j, hf);
+      for (int jj = k + 1; jj < i; ++jj) acc = block_mma(acc, blk(i, jj), LP, 1, blk(k, jj), 1, LP, j, hf);
+      float* out = blk(k, i);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) out[j * LP + acc_row(r, hf)] = -acc[r];
+    }
+    __syncthreads();
+  }
+
+  // ---- 3. M = Y^T Y: block (ba, bb) = sum_{R >= max(ba, bb)} Y_R,ba^T Y_R,bb, where
+  // Y_R,c[r][x] is blk(c, c)[r][x] for R = c and blk(c, R)[x][r] for R > c
+  floatx16 macc[PER_WAVE];
 #pragma unroll
   for (int x = 0; x < PER_WAVE; ++x) {
-    acc[x] = floatx16{};
-    const int blk = w * PER_WAVE + x;
-    if (blk < NBLK) {
-      const int ba = blk / NB, bb = blk % NB;
-      for (int s = 0; s < D / 2; ++s) {
-        const float av = Xs[(2 * s + hf) * LP + 32 * ba + j];
-        const float bv = Xs[(2 * s + hf) * LP + 32 * bb + j];
-        acc[x] = mfma_f32(av, bv, acc[x]);
+    macc[x] = floatx16{};
+    const int bk = w * PER_WAVE + x;
+    if (bk < NBLK) {
+      const int ba = bk / NB, bb = bk % NB;
+      for (int R = ba > bb ? ba : bb; R < NB; ++R) {
+        const float* xa = R == ba ? blk(ba, ba) : blk(ba, R);
+        const int xr = R == ba ? 1 : LP, xm = R == ba ? LP : 1;
+        const float* zb = R == bb ? blk(bb, bb) : blk(bb, R);
+        const int zm = R == bb ? LP : 1, zc = R == bb ? 1 : LP;
+        macc[x] = block_mma(macc[x], xa, xr, xm, zb, zm, zc, j, hf);
       }
     }
   }
   __syncthreads();   // every read of Y done
 #pragma unroll
   for (int x = 0; x < PER_WAVE; ++x) {
-    const int blk = w * PER_WAVE + x;
-    if (blk < NBLK) {
-      const int ba = blk / NB, bb = blk % NB;
+    const int bk = w * PER_WAVE + x;
+    if (bk < NBLK) {
+      const int ba = bk / NB, bb = bk % NB;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = 32 * ba + 8 * (r >> 2) + 4 * hf + (r & 3);
-        Xs[row * LP + 32 * bb + j] = acc[x][r];
-        Gp[row * D + 32 * bb + j] = acc[x][r];
+        const int row = 32 * ba + acc_row(r, hf);
+        As[row * LP + 32 * bb + j] = macc[x][r];
+        Gp[row * D + 32 * bb + j] = macc[x][r];
       }
     }
   }
   __syncthreads();
 
-  // ---- 3. C = beta B M  (C[a][b] = beta sum_k B[a][k] M[k][b])
+  // ---- 4. C = beta B M  (C[a][b] = beta sum_k B[a][k] M[k][b]).  Lane (j, hf)
+  // reads 16 bytes of row j of B at a time, k = 8 u + 4 hf .. + 3, and MFMA 4 u + e
+  // takes k = 8 u + 4 hf + e on both operands (the reduction in another order).
+  floatx16 acc[PER_WAVE];
 #pragma unroll
   for (int x = 0; x < PER_WAVE; ++x) {
-    const int blk = w * PER_WAVE + x;
+    const int bk = w * PER_WAVE + x;
     acc[x] = floatx16{};
-    if (blk < NBLK) {
-      const int ba = blk / NB, bb = blk % NB;
-      for (int s = 0; s < D / 2; ++s) {
-        const float av = Bp[(32 * ba + j) * D + 2 * s + hf];
-        const float bv = Xs[(2 * s + hf) * LP + 32 * bb + j];
-        acc[x] = mfma_f32(av, bv, acc[x]);
+    if (bk < NBLK) {
+      const int ba = bk / NB, bb = bk % NB;
+      const float* brow = Bp + (size_t)(32 * ba + j) * D + 4 * hf;
+      for (int u = 0; u < D / 8; ++u) {
+        const float4 a4 = *reinterpret_cast<const float4*>(brow + 8 * u);
+        const float* mcol = As + (8 * u + 4 * hf) * LP + 32 * bb + j;
+        acc[x] = mfma_f32(a4.x, mcol[0], acc[x]);
+        acc[x] = mfma_f32(a4.y, mcol[LP], acc[x]);
+        acc[x] = mfma_f32(a4.z, mcol[2 * LP], acc[x]);
+        acc[x] = mfma_f32(a4.w, mcol[3 * LP], acc[x]);
       }
     }
   }
   __syncthreads();   // every read of B done before C overwrites it
 #pragma unroll
   for (int x = 0; x < PER_WAVE; ++x) {
-    const int blk = w * PER_WAVE + x;
-    if (blk < NBLK) {
-      const int ba = blk / NB, bb = blk % NB;
+    const int bk = w * PER_WAVE + x;
+    if (bk < NBLK) {
+      const int ba = bk / NB, bb = bk % NB;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = 32 * ba + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const int row = 32 * ba + acc_row(r, hf);
         Bp[row * D + 32 * bb + j] = b * acc[x][r];
       }
     }
@@ -532,7 +605,7 @@ hipError_t launch_gram_f32(const float* k, const float* v, int F, int N, int H, 
 
 template <int D>
 static hipError_t factor_d(float* G, float* B, const float* beta, int F, int H, hipStream_t st) {
-  const size_t lds = ((size_t)D * (D + 1) + 4 * D) * sizeof(float);
+  const size_t lds = ((size_t)D * (D + 1) + 64) * sizeof(float);
   static std::atomic<unsigned long long> attr_done{0};
   hipError_t e = set_max_lds_once(reinterpret_cast<const void*>(&factor_kernel<D>), (int)lds, &attr_done);
   if (e != hipSuccess) return e;

@@ -60,6 +60,8 @@ def rel_err(x, ref, head_axis=2):
         b = np.take(ref, h, axis=head_axis)
         nb = np.linalg.norm(b)
         e = np.linalg.norm(a - b) / nb if nb > 0 else np.linalg.norm(a - b)
+        if not np.isfinite(e):
+            return float("inf")      # NaN / Inf anywhere fails (max() would skip a NaN)
         worst = max(worst, e)
     return worst
 
