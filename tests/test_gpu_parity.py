@@ -159,6 +159,35 @@ def test_identity_keys_ema_states():
         compare_full(inp, got, ref, prec)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_ill_conditioned_keys_states(d):
+    # Every token of a frame carries one key direction plus 1e-3 noise, so A_t =
+    # I + beta_t G_t has a condition number near 1 + beta_t N (about 200 here): the
+    # per-frame factorisation in fp32 loses accuracy in proportion to it (relative
+    # error of order kappa 2^-24 in M_t, and so in the states).  The states are held
+    # to 32 kappa 2^-24, kappa the largest over frames and heads.
+    F, N, H = 14, 256, 2
+    rng = np.random.default_rng(5)
+    base = rng.standard_normal((F, 1, H, d))
+    k = base + 1e-3 * rng.standard_normal((F, N, H, d))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    for prec in ("fp32", "bf16"):
+        inp = Inputs(F, N, H, d, prec, seed=5, k_override=torch.from_numpy(k))
+        k64 = inp.host64("k")
+        beta = inp.beta.numpy().astype(np.float64)
+        kappa = max(np.linalg.cond(np.eye(d) + beta[t, h] * k64[t, :, h, :].T @ k64[t, :, h, :])
+                    for t in range(1, F - 1) for h in range(H))
+        tol = 32 * kappa * 2.0 ** -24
+        say(f"case ill-conditioned keys F={F} N={N} d={d} {prec}: kappa {kappa:.0f}, tol {tol:.2e}")
+        Sf, Sb = vdn.vda_states(inp.dk, inp.dv, inp.dbeta, precision=PREC[prec])
+        torch.cuda.synchronize()
+        rSf, rSb = orc.vda_states(k64, inp.host64("v"), beta)
+        es, eb = _states_err(Sf, rSf), _states_err(Sb, rSb)
+        say(f"  S_fwd {es:.3e}  S_bwd {eb:.3e}")
+        assert kappa > 100        # the case is what it says
+        assert es <= tol and eb <= tol
+
+
 MID = (45, 1024, 16, 128)
 
 
