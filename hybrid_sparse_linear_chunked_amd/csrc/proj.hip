@@ -7,9 +7,13 @@
 // Workgroup tile 256 (M) x 256 (N), 8 waves, K in steps of 64.  Both operand tiles
 // go global -> LDS by 16-byte direct loads (no staging registers) into rows with
 // one 16-byte padding chunk each (144-byte pitch), so 16 consecutive rows read at
-// one chunk hit 16 distinct bank groups; two LDS stages, one barrier per step.
-// Inside a step the operand fragments of sub-step s + 1 are read while the MFMAs
-// of sub-step s run, and the first two sub-steps issue the next step's loads.
+// one chunk hit 16 distinct bank groups; two LDS stages, one barrier per step,
+// placed before the step's last 16-wide sub-step.  Inside a step the operand
+// fragments of sub-step s + 1 are read while the MFMAs of sub-step s run; after
+// the barrier the next step's first fragments are read, and the step after it
+// starts loading into the stage just freed, during the last sub-step's MFMAs
+// (4 % faster than a barrier at the end of the step, after which every wave
+// waits for its first fragments with the matrix core idle).
 // Each wave computes Y^T for 64 rows of B (N) x 128 rows of A (M): the MFMA's A
 // operand is a 32-row block of B, its B operand a 32-row block of A, so each lane
 // ends with 4 consecutive output columns (n) of one output row (m).  The tile
@@ -134,7 +138,13 @@ __global__ __launch_bounds__(64 * PJ_NW, 1) void proj_kernel(const uint16_t* __r
 
   const int nk = K / PJ_TK;
   constexpr int NS = PJ_TK / 16;                       // 16-wide K sub-steps per step
+  // loads of a step issued right after the barrier two steps before, the rest in
+  // the first sub-step of the step before (measured best of 0-5 after the barrier,
+  // and of spreading the rest over two sub-steps)
+  constexpr int LH = PJ_LX / 2;
+  // steps 0 and 1 first (the loop loads step kk + 2 once step kk's stage is free)
   issue(0, 0, 0, PJ_LX);
+  if (nk > 1) issue(1, 1, 0, PJ_LX);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   bf16x8 wf[2][2], af[2][4];
@@ -147,26 +157,38 @@ __global__ __launch_bounds__(64 * PJ_NW, 1) void proj_kernel(const uint16_t* __r
     for (int mb = 0; mb < 4; ++mb)
       af[buf][mb] = *reinterpret_cast<const bf16x8*>(sa + (128 * wm + 32 * mb + j) * PJ_PITCH + 16 * (2 * s + hf));
   };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma_bf16(wf[buf][nb], af[buf][mb], acc[nb][mb]);
+  };
+  read(smem, 0, 0);
+  // The step's barrier sits before its last sub-step: by then every fragment of
+  // the step is read (the last sub-step's during the one before), so the barrier
+  // frees the stage and publishes the next step's loads; the next step's first
+  // fragments are then read, and step kk + 2's loads issued into the freed stage,
+  // while the last sub-step's MFMAs run (a barrier after the last sub-step leaves
+  // the matrix cores idle while all waves read their first fragments at once).
   for (int kk = 0; kk < nk; ++kk) {
-    const bool ld = kk + 1 < nk;
     const unsigned char* sa = smem + (kk & 1) * PJ_STAGE;
-    read(sa, 0, 0);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+    for (int s = 0; s < NS - 1; ++s) {
       __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): sub-step s's fragments
-      if (s + 1 < NS) read(sa, s + 1, (s + 1) & 1);
-      // the next step's loads, half in each of the first two sub-steps (measured
-      // 2-3 % faster than all in the first, or a quarter in each)
-      if (ld && s < 2) issue((kk + 1) & 1, kk + 1, s * PJ_LX / 2, (s + 1) * PJ_LX / 2);
+      read(sa, s + 1, (s + 1) & 1);
+      // the rest of step kk + 1's loads (the first LH went out after the last barrier)
+      if (s == 0 && kk >= 1 && kk + 1 < nk) issue((kk + 1) & 1, kk + 1, LH, PJ_LX);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma_bf16(wf[s & 1][nb], af[s & 1][mb], acc[nb][mb]);
+      mfmas(s & 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next step landed
-    __syncthreads();                 // ... and every wave's; this step's reads done
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's last fragments read, its loads of step kk + 1 landed
+    __syncthreads();                 // ... and every wave's
+    if (kk + 2 < nk) issue(kk & 1, kk + 2, 0, LH);
+    if (kk + 1 < nk) read(smem + ((kk + 1) & 1) * PJ_STAGE, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas((NS - 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // the output tile goes through LDS (free after the last step's barrier) so that
