@@ -73,7 +73,7 @@ extern "C" {
                                       in VDN_PREC_BF16_FP8QK, and P.V with v coded per head
                                       the same way (power-of-two scale, prescale 1) and the
                                       probabilities rounded to E4M3 after the running-max
-                                      shift (row sums from the unrounded values); the VDA
+                                      shift (the row sums add the same rounded values); the VDA
                                       branch and the merge as bf16.  d = 64 or 128;
                                       vdn_hybrid_attn, vdn_hybrid_attn_noalloc,
                                       vdn_softmax_branch, vdn_vda_states and vdn_vda_linear
