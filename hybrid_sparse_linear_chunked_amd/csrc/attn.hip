@@ -1226,6 +1226,310 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   }
 }
 
+// ============================================================ attention, full fp8, two groups of waves
+// With P.V on E4M3 codes a tile costs about as much vector work (the softmax of
+// 64 keys: maxima, exponentials, E4M3 conversions) as matrix work (Q.K^T and P.V
+// on E4M3 codes, the row sums), and a wave's vector instructions do not issue
+// under its own MFMAs (accumulators in VGPRs): the two waves that share a SIMD
+// have to take turns on the two units.  With one barrier per tile
+// (attn_lds_kernel) they start every tile together and their softmaxes collide.
+// Here the workgroup advances in segments separated by one barrier; in segment k
+//   waves 0-3 (one per SIMD): P.V of tile k-1 and Q.K^T of tile k, then the
+//                             softmax of tile k;
+//   waves 4-7:                the softmax of tile k-1, then P.V of tile k-1 and
+//                             Q.K^T of tile k,
+// so in each half of a segment one wave of a SIMD issues MFMAs while the other
+// runs its softmax.  Every wave takes its tiles in order with the same arithmetic
+// as attn_lds_kernel (the outputs are bitwise equal).  Segment k reads tiles k-1
+// and k and loads tile k+1 (four LDS stages).  The compiler makes a wave wait for
+// its own direct loads before its next LDS read, so waves 4-7 issue all of a
+// tile's loads at the start of a segment, before their softmax, and their first
+// operand read comes a softmax later.  Plain video layer (no extra tokens, no
+// split output).
+
+// The softmax of one 64-key tile: scores s (already s - m in log2 units) of the
+// wave's 32 queries, lazy running-max raise (rescaling o and the row sums), then
+// the E4M3 probabilities in pf.  Cursor: tile sm_t, its 64-key block sm_b of the
+// frame.
+template <int NDB>
+__device__ __forceinline__ void pp_softmax(floatx16 (&s)[2], floatx16 (&o)[NDB], floatx16& nm, floatx16& lsum,
+                                           intx8& pf, float& m_run, int& sm_t, int& sm_b, int N, int nb, int hf) {
+  const int nvalid = min(BK, N - BK * sm_b);
+  if (++sm_b == nb) sm_b = 0;
+  if (nvalid < BK) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (key >= nvalid) s[kb][r] = -INFINITY;
+      }
+  }
+  float mx = __builtin_fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+  for (int e = 1; e < 16; ++e) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[0][e]), s[1][e]);
+  const bool first = sm_t == 0;
+  if (first || __any(mx > kLazy)) {
+    mx = pair_max(mx);
+    const float dm = first ? mx : __builtin_fmaxf(mx, 0.f);
+    if (!first) {
+      const float alpha = __builtin_amdgcn_exp2f(-dm);
+      lsum *= alpha;
+#pragma unroll
+      for (int x = 0; x < NDB; ++x) o[x] *= alpha;
+    }
+    m_run += dm;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] -= dm;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nm[r] = -m_run;
+  }
+  asm volatile("" : "+v"(nm));
+  // lane (j, hf) holds keys 32 kb + 8 (r / 4) + 4 hf + r % 4: bytes 16 kb + r
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int kb = t >> 2, r0 = 4 * (t & 3);
+    const float p0 = __builtin_amdgcn_exp2f(s[kb][r0]), p1 = __builtin_amdgcn_exp2f(s[kb][r0 + 1]);
+    const float p2 = __builtin_amdgcn_exp2f(s[kb][r0 + 2]), p3 = __builtin_amdgcn_exp2f(s[kb][r0 + 3]);
+    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+    wd = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
+    pf[t] = wd;
+  }
+  ++sm_t;
+}
+
+template <int D>
+__global__ __launch_bounds__(512, 2) void attn_pp_kernel(AttnArgs a) {
+  using Cfg = LdsCfg<D, 3>;
+  constexpr int NW = 8, NDB = D / 32, NSTG = 4, NQK = 2 * Cfg::QSTEPS;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31, hf = lane >> 5;
+  const bool lead = w < NW / 2;          // matrix half of a segment first
+  // waves 4-7 (softmax first) issue first when both waves of a SIMD are ready
+  // (same-box A/B at the long stream: 306.0 ms against 352.5 with no priority and
+  // 354.1 with waves 0-3 first; priorities switched with the phase: 335-355 ms)
+  if (!lead) __builtin_amdgcn_s_setprio(1);
+  const int F = a.F, N = a.N, H = a.H;
+  const size_t rs = (size_t)H * D;       // token stride (elements; one byte each as codes)
+  const int nb = (N + BK - 1) / BK;
+  // the item from the queues (one thread takes it, one LDS word hands it over)
+  int* slot = reinterpret_cast<int*>(smem + NSTG * Cfg::STAGE);
+  if (tid == 0) *slot = acquire_item(a);
+  __syncthreads();
+  const int pk = __builtin_amdgcn_readfirstlane(*slot);
+  if (pk < 0) return;
+  const int Mi = a.na * a.qt_anchor * a.nsplit + a.tiles_per_head;
+  const int hh0 = pk / Mi;
+  const Item it = uniform_item(decode_item_at(a, hh0, pk - hh0 * Mi));
+  const int h = it.h;
+  const int ntiles = it.nslots * nb;
+
+  // ---- Q operand fragments (E4M3 codes carrying log2(e)/sqrt(d)), resident
+  const int qi = 32 * w + j;
+  const bool qvalid = qi < it.q_rows;
+  const size_t qoff = (size_t)(it.q_tok0 + qi) * rs + (size_t)h * D;
+  intx8 q8f[Cfg::QSTEPS];
+#pragma unroll
+  for (int st = 0; st < Cfg::QSTEPS; ++st) {
+    if (qvalid) {
+      const uint4* p = reinterpret_cast<const uint4*>(a.q8 + qoff + 64 * st + 32 * hf);
+      const uint4 x0 = p[0], x1 = p[1];
+      q8f[st] = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    } else {
+      q8f[st] = intx8{};
+    }
+  }
+  const int sq = a.fexp[h] + 127, sk = a.fexp[H + h] + 127, sv = a.fexp[2 * H + h] + 127;
+
+  // ---- global -> LDS tile loads by waves 4-7: load ii of a tile is issued by wave
+  // 4 + ii % 4 as its load ii / 4; lane L of load ii fills LDS chunk 64 ii + L (the
+  // padded rows of attn_lds_kernel)
+  auto frame_of = [&](int fslot) {
+    return it.mode == 0 ? it.k_f0 + fslot : chunk_key_frame(fslot, it.wf, it.we, F);
+  };
+  constexpr int NL = NW / 2;
+  const int wl = w & (NL - 1);
+  constexpr int KX = (Cfg::K_INSTR + NL - 1) / NL, VX = (Cfg::V_INSTR + NL - 1) / NL;
+  // (the lambda reaches the offsets through pointers: clang drops the host launch
+  // stub of a kernel template whose lambda captures an array sized by a dependent
+  // constant)
+  LaneOffsets<KX, VX> lo;
+  uint32_t* koff = lo.koff;
+  uint32_t* voff = lo.voff;
+#pragma unroll
+  for (int x = 0; x < KX; ++x) {
+    const int q = 64 * (x * NL + wl) + lane;
+    const int row = q / (Cfg::KCH + 1), c = min(q % (Cfg::KCH + 1), Cfg::KCH - 1);
+    koff[x] = (uint32_t)(row * rs) + 16u * c;
+  }
+#pragma unroll
+  for (int x = 0; x < VX; ++x) {
+    const int q = 64 * (x * NL + wl) + lane;
+    const int row = min(q / (Cfg::VCH + 1), D - 1), c = min(q % (Cfg::VCH + 1), Cfg::VCH - 1);
+    voff[x] = (uint32_t)(row * (16 * Cfg::VCH) + 16 * c);
+  }
+  int ld_slot = 0, ld_b = 0, ld_f = frame_of(0), ldt = 0;
+  // waves 4-7: their share of tile ldt, into its stage (every wave keeps the cursor)
+  auto issue_tile = [&]() {
+    if (!lead) {
+      unsigned char* sbase = smem + (ldt & (NSTG - 1)) * Cfg::STAGE;
+      const int nvalid = min(BK, N - BK * ld_b);
+      const unsigned char* kt = a.k8 + ((size_t)ld_f * N + BK * ld_b) * rs + (size_t)h * D;
+      // the resource ends with the frame: rows past its end read as zeros (masked)
+      const __amdgpu_buffer_rsrc_t krsrc = make_rsrc(kt, (uint32_t)(nvalid * rs));
+#pragma unroll
+      for (int x = 0; x < KX; ++x) {
+        if (x * NL + wl >= Cfg::K_INSTR) break;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_ptr)(sbase + 1024 * (x * NL + wl)), 16, koff[x], 0,
+                                                 0, 0);
+      }
+      const unsigned char* vsrc =
+          reinterpret_cast<const unsigned char*>(a.vt) + (((size_t)h * F + ld_f) * nb + ld_b) * (size_t)(D * BK);
+      const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vsrc, (uint32_t)(D * BK));
+#pragma unroll
+      for (int x = 0; x < VX; ++x) {
+        if (x * NL + wl >= Cfg::V_INSTR) break;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void_ptr)(sbase + Cfg::K_BYTES + 1024 * (x * NL + wl)),
+                                                 16, voff[x], 0, 0, 0);
+      }
+    }
+    ++ldt;
+    if (++ld_b == nb) {
+      ld_b = 0;
+      ld_f = frame_of(++ld_slot);
+    }
+  };
+
+  issue_tile();                      // ntiles >= 1
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  floatx16 o[NDB];
+#pragma unroll
+  for (int x = 0; x < NDB; ++x) o[x] = floatx16{};
+  float m_run = 0.f;
+  floatx16 lsum = floatx16{};        // row sums from the all-ones MFMA (every element)
+  floatx16 nm = floatx16{};          // -m in every element: the Q.K^T accumulator start
+  floatx16 s[2];                     // scores of the tile whose softmax is next
+  intx8 pf = intx8{};                // E4M3 probabilities of the tile whose P.V is next
+  int sm_t = 0, sm_b = 0;            // softmax cursor: tile, its 64-key block in the frame
+
+  for (int k = 0; k <= ntiles; ++k) {
+    if (!lead && k + 1 < ntiles) issue_tile();     // tile k + 1
+    if (!lead && k > 0) pp_softmax<NDB>(s, o, nm, lsum, pf, m_run, sm_t, sm_b, N, nb, hf);   // tile k - 1
+    {
+      // P.V of tile k - 1 (probabilities from the softmax before it): the V^T
+      // operands read together, then the MFMAs; then Q.K^T of tile k into s
+      const unsigned char* vbase = smem + ((k - 1) & (NSTG - 1)) * Cfg::STAGE + Cfg::K_BYTES;
+      const unsigned char* kbase = smem + (k & (NSTG - 1)) * Cfg::STAGE;
+      if (k > 0) {
+        intx8 vf8[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) vf8[db] = Cfg::vfrag8(vbase, db, j, hf);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = mfma_fp8_scaled(vf8[db], pf, o[db], sv, 127);
+        constexpr int kOne = 0x38383838;    // E4M3 1.0 in every byte
+        lsum = mfma_fp8_scaled(intx8{kOne, kOne, kOne, kOne, kOne, kOne, kOne, kOne}, pf, lsum, 127, 127);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (k < ntiles) {
+        intx8 kf[NQK];
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) kf[i] = Cfg::kfrag(kbase, i, j, hf);
+        s[0] = nm;
+        s[1] = nm;
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) s[i & 1] = mfma_fp8_scaled(kf[i], q8f[i >> 1], s[i & 1], sk, sq);
+      }
+    }
+    if (lead && k < ntiles) pp_softmax<NDB>(s, o, nm, lsum, pf, m_run, sm_t, sm_b, N, nb, hf);   // tile k
+    // end of the segment: this wave's loads of tile k + 1 have landed and its LDS
+    // reads are done; the barrier publishes tile k + 1 and frees tile k - 1's stage.
+    // (A plain s_barrier: __syncthreads' fence adds nothing here.)
+    __builtin_amdgcn_s_waitcnt(0x0070);            // vmcnt(0) lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+  }
+
+  // ---- epilogue (as attn_lds_kernel's video path): readout + gated merge for
+  // chunk items, the unnormalised state for the anchor rows' key slices
+  const float l_tot = lsum[0];
+  constexpr int WCH = D / 8;
+  constexpr int WP = 16 * (WCH + 1);
+  constexpr int W_INSTR = (D * (WCH + 1) + 63) / 64;
+  static_assert(1024 * W_INSTR <= NSTG * Cfg::STAGE, "W fits in the LDS stages");
+  using KArgs = const __attribute__((address_space(4))) AttnArgs*;
+  KArgs kargs = (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kargs));
+  const uint16_t* Wp = kargs->W;
+  const bool lin = it.split < 0 && Wp != nullptr;   // workgroup-uniform
+  float inv = 1.f / l_tot;
+  if (lin) {
+    const int chunk = it.q_tok0 / N / kChunk;
+    const uint16_t* wsrc = Wp + ((size_t)chunk * H + h) * (size_t)(D * D);
+    const __amdgpu_buffer_rsrc_t wrsrc = make_rsrc(wsrc, (uint32_t)(D * D * 2));
+#pragma unroll
+    for (int x = 0; x < (W_INSTR + NW - 1) / NW; ++x) {
+      if (x * NW + w >= W_INSTR) break;
+      const int q = 64 * (x * NW + w) + lane;
+      const int row = q / (WCH + 1), c = min(q % (WCH + 1), WCH - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (lds_void_ptr)(smem + 1024 * (x * NW + w)), 16,
+                                               (uint32_t)(row * 2 * D + 16 * c), 0, 0, 0);
+    }
+    // q rows as stored (the resident fragments are E4M3 codes)
+    constexpr int QS = D / 16;
+    bf16x8 qr[QS];
+    const uint16_t* qrow = static_cast<const uint16_t*>(kargs->q) + qoff;
+#pragma unroll
+    for (int st = 0; st < QS; ++st) qr[st] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * st + 8 * hf) : bf16x8{};
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      floatx16 acc = floatx16{};
+#pragma unroll
+      for (int st = 0; st < QS; ++st)
+        acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(smem + (32 * db + j) * WP + 16 * (2 * st + hf)), qr[st], acc);
+      // (the rounding order of attn_lds_kernel's full-fp8 epilogue)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = fmaf(acc[r], 1.f, o[db][r] * inv);
+    }
+    inv = 1.f;
+  }
+  if (!qvalid) return;
+  if (it.split < 0) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * db + 8 * g + 4 * hf;
+        const uint2 v2 = make_uint2(pack_bf16x2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
+                                    pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(kargs->O) + qoff + dd) = v2;
+      }
+  } else {
+    const int n = it.q_tok0 - (it.anchor_idx == 0 ? 0 : (F - 1) * N) + qi;
+    const size_t row = (((size_t)it.split * H + h) * kargs->na + it.anchor_idx) * N + n;
+    float* po = kargs->part_O + row * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * db + 8 * g + 4 * hf;
+        *reinterpret_cast<float4*>(po + dd) =
+            make_float4(o[db][4 * g + 0], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+      }
+    if (hf == 0) {
+      kargs->part_ml[2 * row + 0] = m_run;
+      kargs->part_ml[2 * row + 1] = l_tot;
+    }
+  }
+}
+
 // ============================================================ combine
 // One thread per (split-merged row, 4 channels).  Rows: [H][na * N + T], the
 // anchor frames' tokens, then the extra tokens'.
@@ -1402,10 +1706,11 @@ static hipError_t attn_lds(const AttnArgs& a, hipStream_t st, bool split) {
   // the tile stages, then one word that hands a queued item to every wave
   constexpr int lds = kLdsStages * LdsCfg<D, PREC>::STAGE + 16;
   if constexpr (PREC == 3) {
-    // fp8 P.V: the plain layer only (no extra tokens, no split output)
+    // fp8 P.V: the plain layer only (no extra tokens, no split output), by the
+    // two-group kernel (4 LDS stages, 8 waves)
     if (split || a.T > 0) return hipErrorInvalidValue;
     static std::atomic<unsigned long long> done8{0};
-    return attn_launch(&attn_lds_kernel<D, PREC, kLdsWaves, false, false>, lds, &done8, a, st, 64 * kLdsWaves, true);
+    return attn_launch(&attn_pp_kernel<D>, 4 * LdsCfg<D, PREC>::STAGE + 16, &done8, a, st, 512, true);
   } else {
   if constexpr (D == 128) {
     // opt-in: the 64-queries-per-wave kernel (half the LDS reads per MFMA, one
