@@ -14,7 +14,13 @@
 //   attn_kernel      flash-style attention: a 128-query tile against the key
 //                    frames of its chunk (or one slice of all frames for anchor
 //                    query frames), K / V^T tiles double-buffered in LDS, online
-//                    softmax in fp32 registers, 32x32 MFMA for Q.K^T and P.V.
+//                    softmax in fp32 registers, 32x32 MFMA for Q.K^T and P.V
+//                    (the fp32 layer).
+//   attn_lds_kernel  the same for bf16 and fp8-q.k I/O with 256-query items from
+//                    per-XCD queues, tiles moved global -> LDS by direct loads,
+//                    and the linear readout + gated merge in its epilogue.
+//   attn_pp_kernel   the full-fp8 path (q.k and P.V on E4M3 codes): two groups of
+//                    waves that take turns on the matrix and vector units.
 //   combine_kernel   log-sum-exp merge of the anchor rows' key slices.
 //   amax / fp8_exp / quant   per-head E4M3 quantiser (power-of-two scales) of
 //                    the fp8 Q.K^T variant.
@@ -706,11 +712,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   // the factor log2(e)/sqrt(d) (rounded once to bf16).  fp8: the q codes carry it
   // (applied before quantisation), and the power-of-two scales of the q and k
   // codes are the MFMA's E8M0 operand scales (sq for Q, sk for K)
-  int sq = 0, sk = 0, sv = 0;
+  int sq = 0, sk = 0;
   if constexpr (FP8) {
     sq = a.fexp[h] + 127;
     sk = a.fexp[H + h] + 127;
-    if constexpr (Cfg::FP8V) sv = a.fexp[2 * H + h] + 127;
   } else {
     const float scale = a.scale_log2;
 #pragma unroll
@@ -728,7 +733,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
     // and L2-miss traffic follow the layout; each path takes the combination
     // measured fastest for it (same-box A/B: bf16 at the 768p workload 247.6 vs
     // 252.4 ms, 255 vs 515 GB past L2; fp8 q.k at the long stream 425.7 vs 441.0 ms,
-    // 308 vs 807 GB; full fp8 340.3 vs 344.2 ms).
+    // 308 vs 807 GB).
     if constexpr (PREC == 2) return it.mode == 0 ? it.k_f0 + slot : chunk_key_frame_sel(slot, it.wf, it.we, F);
     else return it.mode == 0 ? it.k_f0 + slot : chunk_key_frame(slot, it.wf, it.we, F);
   };
@@ -774,12 +779,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       if (x * NW + w >= Cfg::K_INSTR) break;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_ptr)(sbase + 1024 * (x * NW + w)), 16, koff[x], 0, 0, 0);
     }
-    // (fp8 P.V: vt holds the E4M3 codes of v, one byte per element)
-    constexpr int VEB = Cfg::FP8V ? 1 : 2;
     const unsigned char* vsrc =
         XT && f == F ? reinterpret_cast<const unsigned char*>(a.vtx + ((size_t)h * a.nbx + b) * (size_t)(D * BK))
-                     : reinterpret_cast<const unsigned char*>(a.vt) + (((size_t)h * F + f) * nb + b) * (size_t)(D * BK * VEB);
-    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vsrc, (uint32_t)(D * BK * VEB));
+                     : reinterpret_cast<const unsigned char*>(a.vt) + (((size_t)h * F + f) * nb + b) * (size_t)(D * BK * 2);
+    const __amdgpu_buffer_rsrc_t vrsrc = make_rsrc(vsrc, (uint32_t)(D * BK * 2));
 #pragma unroll
     for (int x = 0; x < VX; ++x) {
       if (KX + x < x0 || KX + x >= x1) continue;
@@ -808,10 +811,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   // MFMAs leave s - m and the exponent needs no VALU op; m is finite from the
   // start and the first tile sets it to that tile's maximum
   float m_run = 0.f, l_run = 0.f;
-  // full fp8: the row sums come from the matrix core, one more 64-deep MFMA per tile
-  // with an all-ones A operand, so they are the sums of the rounded probabilities
-  // that P.V uses (every element of lsum holds the lane's query's whole sum)
-  floatx16 lsum = floatx16{};
   floatx16 nm = floatx16{};      // -m in every element: the first Q.K^T accumulator input
   if constexpr (XI) {
     // start from the state after the extra tokens' keys (l on the first half-wave
@@ -895,7 +894,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       if (bt + 1 < NQB) {
 #pragma unroll
         for (int x = 0; x < QB; ++x) kf[(bt + 1) & 1][x] = Cfg::kfrag(sbase, (bt + 1) * QB + x, j, hf);
-      } else if constexpr (!Cfg::FP8V) {
+      } else {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) va[0][db] = Cfg::vfrag(vbase, 0, db, j, hf);
       }
@@ -939,7 +938,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
         if (!first) {
           const float alpha = __builtin_amdgcn_exp2f(-dm);
           l_run *= alpha;
-          if constexpr (Cfg::FP8V) lsum *= alpha;
 #pragma unroll
           for (int x = 0; x < NDB; ++x) o[x] *= alpha;
         }
@@ -956,33 +954,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
     // exponent of a score: the scores are already s - m in log2 units
     auto expo = [&](float x) { return __builtin_amdgcn_exp2f(x); };
 
-    if constexpr (Cfg::FP8V) {
-      // ---- O^T += V^T P^T on E4M3 codes: one 64-deep MFMA per 32-channel block
-      // covers the tile's 64 keys.  Lane (j, hf) holds the probabilities of query j
-      // for keys 32 kb + 8 (r / 4) + 4 hf + r % 4 (kb = 0, 1; r = 0..15), packed as
-      // bytes 16 kb + r of its B operand; the vt8 layout puts the same keys at the
-      // same bytes of the lane's V^T operand.  P is in (0, 2^kLazy], inside E4M3's
-      // range.  The row sums take the same rounded values (the all-ones MFMA into
-      // lsum), replacing 32 vector adds per tile with one MFMA.
-      intx8 vf8[NDB];
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) vf8[db] = Cfg::vfrag8(vbase, db, j, hf);
-      intx8 pf;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int kb = t >> 2, r0 = 4 * (t & 3);
-        const float p0 = expo(s[kb][r0]), p1 = expo(s[kb][r0 + 1]);
-        const float p2 = expo(s[kb][r0 + 2]), p3 = expo(s[kb][r0 + 3]);
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-        wd = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
-        pf[t] = wd;
-      }
-      lds_wait_all();
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] = mfma_fp8_scaled(vf8[db], pf, o[db], sv, 127);
-      constexpr int kOne = 0x38383838;      // E4M3 1.0 in every byte
-      lsum = mfma_fp8_scaled(intx8{kOne, kOne, kOne, kOne, kOne, kOne, kOne, kOne}, pf, lsum, 127, 127);
-    } else {
     // ---- O^T += V^T P^T, one group of 16 keys per batch; the probabilities of
     // the next group are formed on the VALU while this group's MFMAs run, and
     // the row sum l takes the same bf16 values, two per v_dot2_f32_bf16
@@ -1022,7 +993,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run += psum;
-    }
 
     if ((t & (AHEAD - 1)) == AHEAD - 1 || t + 1 == ntiles) {
       __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next tiles landed
@@ -1031,7 +1001,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   }
 
   // ---- epilogue
-  const float l_tot = Cfg::FP8V ? lsum[0] : pair_sum(l_run);
+  const float l_tot = pair_sum(l_run);
   // Linear-branch readout and gated merge, fused (besthub article "VDN-H3
   // Generates 14-Second 768p Video ...", Hybrid Attention Architecture: the gated
   // linear output is added to the softmax output): every query row of a chunk
@@ -1071,11 +1041,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
   }
   const uint16_t* Wp = kargs->W;
   const bool lin = it.split < 0 && Wp != nullptr;    // workgroup-uniform
-  // fp8 paths: q rows as stored (the resident fragments are E4M3 codes); the
-  // fp8-q.k path loads them beside the W tile, the full-fp8 path at the readout
-  // (the shape measured faster for each, see frame_of)
-  constexpr bool EARLY_Q = PREC == 2;
-  bf16x8 q8r[EARLY_Q ? D / 16 : 1];
+  // fp8 q.k: q rows as stored (the resident fragments are E4M3 codes), loaded
+  // beside the W tile
+  bf16x8 q8r[FP8 ? D / 16 : 1];
   if (lin) {
     const int chunk = it.q_tok0 / N / kChunk;      // chunk of the item's first (and every) row
     const uint16_t* wsrc = Wp + ((size_t)chunk * H + h) * (size_t)(D * D);
@@ -1089,7 +1057,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, (lds_void_ptr)(smem + 1024 * (x * NW + w)), 16,
                                                (uint32_t)(row * 2 * D + 16 * c), 0, 0, 0);
     }
-    if constexpr (EARLY_Q) {
+    if constexpr (FP8) {
       const uint16_t* qrow = static_cast<const uint16_t*>(kargs->q) + (size_t)(it.q_tok0 + qi) * rs + (size_t)h * D;
 #pragma unroll
       for (int s = 0; s < D / 16; ++s)
@@ -1106,15 +1074,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
       constexpr int QS = D / 16;
       bf16x8 qr[QS];
       float us;
-      if constexpr (EARLY_Q) {
+      if constexpr (FP8) {
 #pragma unroll
         for (int s = 0; s < QS; ++s) qr[s] = q8r[s];
-        us = 1.f;
-      } else if constexpr (FP8) {
-        const uint16_t* q = static_cast<const uint16_t*>(a.q);
-#pragma unroll
-        for (int s = 0; s < QS; ++s)
-          qr[s] = qvalid ? *reinterpret_cast<const bf16x8*>(q + qoff + 16 * s + 8 * hf) : bf16x8{};
         us = 1.f;
       } else {
 #pragma unroll
@@ -1156,15 +1118,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
     constexpr int QS = D / 16;
     bf16x8 qr[QS];
     float us;
-    if constexpr (EARLY_Q) {
+    if constexpr (FP8) {
 #pragma unroll
       for (int s = 0; s < QS; ++s) qr[s] = q8r[s];
-      us = 1.f;
-    } else if constexpr (FP8) {
-      const uint16_t* q = static_cast<const uint16_t*>(a.q);
-#pragma unroll
-      for (int s = 0; s < QS; ++s)
-        qr[s] = qvalid ? *reinterpret_cast<const bf16x8*>(q + qoff + 16 * s + 8 * hf) : bf16x8{};
       us = 1.f;
     } else {
 #pragma unroll
@@ -1179,7 +1135,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_lds_kernel(AttnArgs a) {
         acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(smem + (32 * db + j) * WP + 16 * (2 * s + hf)), qr[s], acc);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if constexpr (EARLY_Q) o[db][r] = fmaf(o[db][r], inv, acc[r]);
+        if constexpr (FP8) o[db][r] = fmaf(o[db][r], inv, acc[r]);
         else o[db][r] = fmaf(acc[r], us, o[db][r] * inv);
       }
     }
