@@ -32,6 +32,11 @@ medians over the timed steps.  Besides the contract fields the line carries
                 (the O_lin = W q entry point) against 8 TB/s;
   cpu_baseline  the fp64 oracle on the host (rank 0, N=1): in full for the three
                 small workloads, else on a bounded sample extrapolated to a layer.
+With `--vendor-attention` the line also carries `vendor_attention`: torch's fused
+attention (its flash / memory-efficient kernels only, never the math fallback) on
+the dense sub-problem of one interior chunk (all heads; the chunk's 5 query frames
+against its 17 key frames, no mask), timed on the same device beside the layer as
+a same-box library reference for the attention kernel's TFLOP/s.
 """
 from __future__ import annotations
 
@@ -214,6 +219,51 @@ def cpu_baseline_sampled(F, N, H, d, fp32, tokens=2560):
     }
 
 
+def vendor_attention(F, N, H, d, dev, reps):
+    """torch's fused scaled-dot-product attention (flash, else memory-efficient
+    kernel; the math fallback is excluded) on one interior chunk's dense problem:
+    5 query frames against 17 key frames (15 window frames + 2 anchors), all heads,
+    bf16, no mask.  FLOP = 4 d H Nq Nk; median of `reps` timed calls after 2."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    nq_f, nk_f = 5, 17
+    if F < 20:
+        return {"skipped": "fewer than 4 chunks"}
+    g = torch.Generator(device=dev).manual_seed(0)
+    Lq, Lk = nq_f * N, nk_f * N
+    qd = torch.randn((1, H, Lq, d), device=dev, dtype=torch.bfloat16, generator=g)
+    kd = torch.randn((1, H, Lk, d), device=dev, dtype=torch.bfloat16, generator=g)
+    vd = torch.randn((1, H, Lk, d), device=dev, dtype=torch.bfloat16, generator=g)
+    flop = 4.0 * d * H * Lq * Lk
+    out = {"shape": {"H": H, "Lq": Lq, "Lk": Lk, "d": d, "dtype": "bf16"}, "flop_per_call": flop}
+    for name, backend in (("flash", SDPBackend.FLASH_ATTENTION), ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            with sdpa_kernel([backend]):
+                for _ in range(2):
+                    torch.nn.functional.scaled_dot_product_attention(qd, kd, vd)
+                torch.cuda.synchronize()
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(reps)]
+                for a, b in ev:
+                    a.record()
+                    torch.nn.functional.scaled_dot_product_attention(qd, kd, vd)
+                    b.record()
+                torch.cuda.synchronize()
+        except RuntimeError as e:                      # no such kernel for this device / shape
+            print(f"[bench] vendor attention ({name}): {str(e).splitlines()[0]}", file=sys.stderr, flush=True)
+            continue
+        t = statistics.median([a.elapsed_time(b) for a, b in ev])
+        tf = flop / (t * 1e-3) / 1e12
+        out.update({"backend": f"torch scaled_dot_product_attention ({name})", "ms": round(t, 4),
+                    "tflops": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        print(f"[bench] vendor attention ({name}): {t:.3f} ms, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        break
+    else:
+        out["backend"] = None
+    del qd, kd, vd
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,6 +279,9 @@ def main():
     ap.add_argument("--out-proj", type=int, default=0, metavar="D",
                     help="follow the layer with the two branches' output projections to D channels "
                          "(no CPU baseline)")
+    ap.add_argument("--vendor-attention", action="store_true",
+                    help="also time torch's fused attention on one interior chunk's dense sub-problem "
+                         "(a same-box library reference for the attention kernel's TFLOP/s)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (a known-size kernel "
                          "that calibrates the HBM byte counters), then exit")
@@ -444,6 +497,9 @@ def main():
                           "frac": round(pj / PEAK_BF16_TFLOPS, 4), "kernel": "proj_kernel",
                           "flop_per_launch": proj_flop, "kernel_ms": round(pj_ms, 3)}
     del q, k, v, O, ws
+    if args.vendor_attention and not fp32 and T == 0 and Dp == 0:
+        result["vendor_attention"] = vendor_attention(F, N, H, d, dev, reps=5 if big else 10)
+        result["vendor_attention"]["ours_tflops"] = round(achieved, 2)
     if not args.no_cpu_baseline and T == 0 and Dp == 0:
         full = args.config in FULL_ORACLE
         print(f"[bench] timing the oracle ({'whole layer' if full else 'bounded sample'})", file=sys.stderr,
