@@ -287,6 +287,9 @@ def test_w64_kernel_opt_in(precision, monkeypatch):
     (24, 50, 2, 128),     # ragged 64-key tiles and query tile
     (31, 48, 2, 64),      # d = 64, partial last chunk
     (7, 40, 2, 128),      # every chunk sees every frame: no linear states
+    (1, 20, 1, 64),       # one frame, one partial tile: a segment loop of two passes
+    (2, 64, 2, 128),      # two anchor frames, one whole tile each
+    (16, 300, 1, 64),     # several tiles per frame, ragged last tile and query tile
 ])
 def test_full_fp8_layer(cfg):
     F, N, H, d = cfg
