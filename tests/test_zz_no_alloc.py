@@ -15,7 +15,10 @@ from vdn_testlib import TOL, Inputs, oracle_slices, rel_err
 
 pytestmark = pytest.mark.gpu
 
-PREC = {"fp32": vdn.PREC_FP32, "bf16": vdn.PREC_BF16, "bf16_fp8qk": vdn.PREC_BF16_FP8QK}
+PREC = {"fp32": vdn.PREC_FP32, "bf16": vdn.PREC_BF16, "bf16_fp8qk": vdn.PREC_BF16_FP8QK, "fp8": vdn.PREC_FP8}
+# O against the oracle fed the same E4M3 operands (full fp8: the probabilities'
+# E4M3 rounding bound, as in the full-fp8 parity tests)
+O_TOL = {"fp32": TOL["fp32"], "bf16": TOL["bf16"], "bf16_fp8qk": TOL["bf16"], "fp8": 5e-2}
 
 
 def say(*a):
@@ -41,16 +44,18 @@ def _one(cfg, seed):
     torch.cuda.synchronize()
     bits = torch.int32 if prec == "fp32" else torch.int16
     assert torch.equal(got.view(bits), ref.view(bits)), "no-allocation output differs from vdn_hybrid_attn"
-    rOs, rOl, rO, _, _ = oracle_slices(inp, list(range(F)), list(range(H)), fp8=prec == "bf16_fp8qk")
+    rOs, rOl, rO, _, _ = oracle_slices(inp, list(range(F)), list(range(H)), fp8=prec in ("bf16_fp8qk", "fp8"),
+                                       fp8v=prec == "fp8")
     e = rel_err(got.to(torch.float64).cpu().numpy(), rO)
     say(f"  bitwise equal to vdn_hybrid_attn; O rel_F err {e:.3e}")
-    assert e <= TOL["bf16" if prec == "bf16_fp8qk" else prec]
+    assert e <= O_TOL[prec]
 
 
 @pytest.mark.parametrize("pair", [
     ((30, 256, 8, 64, "bf16"), (22, 100, 2, 64, "bf16")),
     ((31, 48, 2, 64, "bf16_fp8qk"), (12, 40, 1, 64, "bf16_fp8qk")),
     ((26, 65, 2, 128, "fp32"), (20, 16, 2, 32, "fp32")),
+    ((24, 50, 2, 128, "fp8"), (9, 30, 1, 64, "fp8")),
 ])
 def test_noalloc_matches_workspace_entry_two_calls(pair):
     big, small = pair
